@@ -478,3 +478,27 @@ def test_round_bf16_matches_torch():
     ours = inputs.round_bf16(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(ours, ref)
+
+
+def test_selection_uses_only_its_query_group():
+    """Query head hq belongs to KV head hq // G: the selection of KV head 1 is
+    blind to the query heads of group 0 and follows those of group 1.  Group 1's
+    queries all point along e1 and only chunk 2's gist key has an e1 part, so
+    chunk 2 must be KV head 1's top-1; group 0 is random noise."""
+    lay = O.Layout(1, 3, 1, 1, 1)
+    L = 1 + 6 * 4
+    tm = O.type_map(lay, L)
+    d, Hq, Hkv = 8, 4, 2
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((1, L, Hkv, d))
+    k[..., 1] = 0.0
+    k[0, tm.chunk_gists[2][0], 1, 1] = 5.0
+    base = rng.standard_normal((1, L, Hq, d))
+    base[0, :, 2:4, :] = 0.0
+    base[0, :, 2:4, 1] = 3.0
+    res = O.select(lay, tm, base, k, [L - 1], 0.5)
+    assert res["sel"][0, 1, 0, 0] == 2
+    noisy = base.copy()
+    noisy[0, :, 0:2, :] = rng.standard_normal((L, 2, d)) * 10
+    res2 = O.select(lay, tm, noisy, k, [L - 1], 0.5)
+    assert np.array_equal(res["sel"][0, 1], res2["sel"][0, 1])
