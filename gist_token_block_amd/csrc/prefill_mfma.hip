@@ -1,0 +1,332 @@
+// Block-sparse flash-style prefill on bf16 MFMA (gfx950), and the
+// gsa_attn_prefill entry point.
+//
+// Each query row attends to its visible keys (sinks, earlier gists, causal
+// window: UniGist summary, Approach; plus unfolded chunks: Simplified Sparse
+// Attention via Gist Tokens, abstract).  The row's visible keys are walked as
+// stream-ordered 64-key tiles taken from the block-visibility table, so EMPTY
+// tiles cost nothing and only PARTIAL tiles (or short ones) are masked; the
+// grouping of gists into one stream stands in for the gist shift the UniGist
+// summary describes (Approach).
+//
+// Workgroup: 4 waves, 128 query rows of one query head; wave w owns rows
+// [32w, 32w+32).  Per key tile:
+//   * K tile [64 keys][d] staged to LDS row-major; V tile staged transposed
+//     [d][64 keys] so the PV operand reads are contiguous in keys.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so
+//     a lane's 32 logits belong to one query: the row max and sum are in-lane
+//     plus one exchange between the two lane halves.
+//   * Online softmax in base 2 (scale * log2 e folded into one FMA).
+//   * O^T += V^T P^T with the same MFMA; P goes from the S accumulators to
+//     bf16 operands without leaving registers: the k-index of both operands is
+//     mapped to the key each lane already holds.
+// Work order: blockIdx is remapped so that each XCD (blockIdx % 8) runs a
+// contiguous range of (batch, KV head, query tile descending, query head):
+// the query heads sharing a KV head and the neighbouring query tiles, which
+// read the same gist stream, hit the same L2, and the heaviest tiles start
+// first.
+#include "gsa_internal.h"
+
+namespace gsa {
+
+gsa_status launch_prefill_rowwave(const Lay& l, int d, const gsa_tensor& q, const gsa_tensor& k,
+                                  const gsa_tensor& v, const gsa_tensor& o, float* lse, int B, int Hq,
+                                  int Hkv, int q_begin, int q_len, int bm, int nqt, const int* sel,
+                                  const int* selg, const int8_t* table, const int* tile_cnt,
+                                  const int* tile_list, float scale, bool fixed, hipStream_t st);
+
+namespace {
+
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+
+template <int D> struct Cfg {
+  static constexpr int KP = D + 8;       // K tile pitch (elements), rows 16-byte aligned
+  static constexpr int VTP = kBN + 4;    // V^T tile pitch (elements), rows 8-byte aligned
+  static constexpr int KS = D / 16;      // k-steps of the QK product
+  static constexpr int MT = D / 32;      // 32-row output tiles of O^T
+  static constexpr int PPR = D / 8;      // 16-byte pieces per key row
+};
+
+template <typename TO> struct OutStore;
+template <> struct OutStore<float> {
+  __device__ static void put4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+};
+template <> struct OutStore<unsigned short> {
+  __device__ static void put4(unsigned short* p, float a, float b, float c, float d) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  }
+};
+
+template <int D, typename TO>
+__global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
+    Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
+    const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
+    const unsigned short* __restrict__ v, int64_t vsb, int64_t vst, int64_t vsh, TO* __restrict__ o,
+    int64_t osb, int64_t ost, int64_t osh, float* __restrict__ lse, int Hq, int Hkv, int q_begin,
+    int q_len, int nqt, const int* __restrict__ sel, const int* __restrict__ selg,
+    const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
+    const int* __restrict__ tile_list, float c2, int fixed, int total) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) unsigned short Klds[kBN * C::KP];
+  __shared__ __attribute__((aligned(16))) unsigned short VTlds[D * C::VTP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, h2 = lane >> 5;
+
+  // XCD-aware work order
+  const int x = blockIdx.x;
+  const int per = total >> 3, rem = total & 7, xcd = x & 7;
+  const int logical = xcd * per + imin(xcd, rem) + (x >> 3);
+  const int G = Hq / Hkv;
+  int rest = logical;
+  const int gq = rest % G;
+  rest /= G;
+  const int qd = rest % nqt;
+  rest /= nqt;
+  const int h = rest % Hkv;
+  const int b = rest / Hkv;
+  const int qt = nqt - 1 - qd;
+  const int hq = h * G + gq;
+
+  // this lane's query row and its Q^T operands (B operand of S^T = K Q^T)
+  const int r = qt * kBM + wave * 32 + n;
+  const bool rvalid = r < q_len;
+  const int i = q_begin + r;
+  bf16x8 qreg[C::KS];
+  {
+    const unsigned short* qrow = q + b * qsb + (int64_t)imin(r, q_len - 1) * qst + hq * qsh;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * h2 + 16 * ks);
+      if (!rvalid) w = u32x4{0u, 0u, 0u, 0u};
+      qreg[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int* selrow = sel ? sel + (((size_t)b * Hkv + h) * q_len + imin(r, q_len - 1)) * l.k : nullptr;
+  const int* selgrow = selg ? selg + (((size_t)b * Hkv + h) * q_len + imin(r, q_len - 1)) * l.k2 : nullptr;
+
+  const unsigned short* kb = k + b * ksb + h * ksh;
+  const unsigned short* vb = v + b * vsb + h * vsh;
+  const int t = fixed ? 0 : b * Hkv + h;
+  const size_t trow = (size_t)t * nqt + qt;
+  const int cnt = tile_cnt[trow];
+  const int* list = tile_list + trow * l.nkt;
+  const int8_t* codes = table + trow * l.nkt;
+
+  f32x16 oacc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x16{};
+  float m_run = kNegBig, l_run = 0.f;
+
+  for (int idx = 0; idx < cnt; ++idx) {
+    const int kt = list[idx];
+    const int code = codes[kt];
+    int kind, u0, u1;
+    tile_span(l, kt, kind, u0, u1);
+    const int width = u1 - u0;
+
+    // ---- stage K (row-major) and V (transposed) into LDS
+    {
+      constexpr int RPP = kThreads / C::PPR;  // key rows per pass
+#pragma unroll
+      for (int it = 0; it < kBN / RPP; ++it) {
+        const int key = tid / C::PPR + RPP * it;
+        const int piece = tid % C::PPR;
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        if (key < width) {
+          const int p = pos_of(l, kind, u0 + key);
+          w = *reinterpret_cast<const u32x4*>(kb + (int64_t)p * kst + piece * 8);
+        }
+        *reinterpret_cast<u32x4*>(&Klds[key * C::KP + piece * 8]) = w;
+      }
+      if (tid < 16 * C::PPR) {
+        const int rg = tid & 15, pc = tid >> 4;
+        u32x4 w[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int key = 4 * rg + a;
+          w[a] = u32x4{0u, 0u, 0u, 0u};
+          if (key < width) {
+            const int p = pos_of(l, kind, u0 + key);
+            w[a] = *reinterpret_cast<const u32x4*>(vb + (int64_t)p * vst + pc * 8);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int dw = e >> 1;
+          unsigned lo, hi;
+          if (e & 1) {
+            lo = (w[0][dw] >> 16) | (w[1][dw] & 0xffff0000u);
+            hi = (w[2][dw] >> 16) | (w[3][dw] & 0xffff0000u);
+          } else {
+            lo = (w[0][dw] & 0xffffu) | (w[1][dw] << 16);
+            hi = (w[2][dw] & 0xffffu) | (w[3][dw] << 16);
+          }
+          *reinterpret_cast<u32x2*>(&VTlds[(pc * 8 + e) * C::VTP + 4 * rg]) = u32x2{lo, hi};
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T : two 32x32 tiles (keys 0..31, 32..63) x this wave's 32 queries
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Klds[n * C::KP + 8 * h2 + 16 * ks]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Klds[(32 + n) * C::KP + 8 * h2 + 16 * ks]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
+    }
+
+    // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
+    if (code != 2 || width < kBN) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key0 = 8 * (j >> 2) + 4 * h2 + (j & 3);
+        const int key1 = key0 + 32;
+        bool v0 = key0 < width, v1 = key1 < width;
+        if (code != 2) {
+          if (v0) v0 = key_visible(l, i, kind, u0 + key0, pos_of(l, kind, u0 + key0), selrow, selgrow);
+          if (v1) v1 = key_visible(l, i, kind, u0 + key1, pos_of(l, kind, u0 + key1), selrow, selgrow);
+        }
+        if (!v0) s0[j] = -__builtin_inff();
+        if (!v1) s1[j] = -__builtin_inff();
+      }
+    }
+
+    // ---- online softmax (base 2)
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s0[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -m_new));
+      s1[j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -m_new));
+      psum += s0[j] + s1[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
+
+    // P^T operands: step st uses tile st/2, accumulator regs 8(st%2)..+7
+    bf16x8 pk[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const f32x16& src = (st < 2) ? s0 : s1;
+      const int base = 8 * (st & 1);
+      u32x4 w;
+      w[0] = pack_bf16x2(src[base + 0], src[base + 1]);
+      w[1] = pack_bf16x2(src[base + 2], src[base + 3]);
+      w[2] = pack_bf16x2(src[base + 4], src[base + 5]);
+      w[3] = pack_bf16x2(src[base + 6], src[base + 7]);
+      pk[st] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // ---- O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const unsigned short* vrow = &VTlds[(32 * mt + n) * C::VTP];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * st + 4 * h2);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * st + 8 + 4 * h2);
+        const u32x4 w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[st],
+                                                           oacc[mt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds O^T[d][query n], d = 32mt + 8(j/4) + 4h2 + j%4
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (rvalid) {
+    const float inv = 1.f / l_tot;
+    TO* orow = o + b * osb + (int64_t)r * ost + hq * osh;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * mt + 8 * jj + 4 * h2;
+        OutStore<TO>::put4(orow + d0, oacc[mt][4 * jj] * inv, oacc[mt][4 * jj + 1] * inv,
+                           oacc[mt][4 * jj + 2] * inv, oacc[mt][4 * jj + 3] * inv);
+      }
+    }
+    if (lse && h2 == 0) lse[((size_t)b * Hq + hq) * q_len + r] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace
+}  // namespace gsa
+
+using namespace gsa;
+
+extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                       gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                                       const int32_t* sel, const int32_t* sel_groups,
+                                       const int8_t* table, const int32_t* tile_cnt,
+                                       const int32_t* tile_list, int32_t block_m, int32_t block_n,
+                                       float scale, void* stream) {
+  Lay l;
+  gsa_status st = make_lay(layout, seq_len, block_n, &l);
+  if (st != GSA_OK) return st;
+  if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
+  if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
+  if ((st = check_tensor("v", v, d)) != GSA_OK) return st;
+  if ((st = check_tensor("o", o, d)) != GSA_OK) return st;
+  if (q.dtype != k.dtype || q.dtype != v.dtype) return fail(GSA_EINVAL, "q, k, v dtypes differ");
+  if (o.dtype != GSA_F32 && o.dtype != q.dtype) return fail(GSA_EINVAL, "o dtype must be F32 or the input dtype");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(GSA_EINVAL, "bad head counts B=%d Hq=%d Hkv=%d", B, Hq, Hkv);
+  if (d < 8 || d % 8) return fail(GSA_EUNSUPPORTED, "head dim %d (multiple of 8 required)", d);
+  if (!(scale > 0.f)) return fail(GSA_EINVAL, "scale must be > 0");
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (block_m < 1) return fail(GSA_EINVAL, "block_m %d < 1", block_m);
+  const bool fixed = l.k == 0 && l.G2 == 0;
+  if (!fixed && !sel) return fail(GSA_EINVAL, "sel is required when top_k > 0");
+  if (fixed && sel) return fail(GSA_EINVAL, "sel given for the fixed layout");
+  if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is required with two levels");
+  if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
+  if (l.k > 64 || l.k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
+  if (!table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "table pointers are NULL");
+  if (q_len == 0) return GSA_OK;
+  const int nqt = (q_len + block_m - 1) / block_m;
+  hipStream_t s = (hipStream_t)stream;
+  const bool mfma = q.dtype == GSA_BF16 && (d == 64 || d == 128);
+  if (mfma) {
+    if (block_m != kBM || block_n != kBN)
+      return fail(GSA_EINVAL, "bf16 d=%d prefill needs a %dx%d table (got %dx%d)", d, kBM, kBN, block_m, block_n);
+    const long long total = (long long)B * Hkv * nqt * (Hq / Hkv);
+    if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
+    const float c2 = scale * kLog2e;
+#define GSA_MFMA(D, TO)                                                                              \
+  hipLaunchKernelGGL((k_prefill_mfma<D, TO>), dim3((unsigned)total), dim3(kThreads), 0, s, l,         \
+                     (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                \
+                     (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                \
+                     (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr,    \
+                     o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, nqt, sel,      \
+                     sel_groups, table, tile_cnt, tile_list, c2, (int)fixed, (int)total)
+    if (d == 128) {
+      if (o.dtype == GSA_F32) GSA_MFMA(128, float);
+      else GSA_MFMA(128, unsigned short);
+    } else {
+      if (o.dtype == GSA_F32) GSA_MFMA(64, float);
+      else GSA_MFMA(64, unsigned short);
+    }
+#undef GSA_MFMA
+    return launch_status("gsa_attn_prefill (mfma)");
+  }
+  if (block_n > 256) return fail(GSA_EUNSUPPORTED, "block_n %d > 256 on the row-wave path", block_n);
+  return launch_prefill_rowwave(l, d, q, k, v, o, lse, B, Hq, Hkv, q_begin, q_len, block_m, nqt, sel,
+                                sel_groups, table, tile_cnt, tile_list, scale, fixed, s);
+}

@@ -1,0 +1,307 @@
+// Gist scoring and per-KV-group top-k selection (gsa_score_select).
+//
+// A query scores the chunks whose gists all precede it against their gist
+// keys only, and keeps the k best for unfolding (Simplified Sparse Attention
+// via Gist Tokens, abstract); with two levels it first keeps the best groups by
+// their level-2 gists and then the best chunks inside those groups (Forget,
+// Then Recall ... Gist Sparse Attention, abstract).  Score of a candidate for a
+// KV head = mean over the KV group's query heads, and over the candidate's
+// gists, of q.k * scale; the query-head mean is taken first (qbar), which is
+// the same number by linearity.  Order: score descending, then id ascending.
+//
+// One workgroup (4 waves) per (batch, KV head, query row).  Candidates are
+// scored 64 at a time; lanes of a row group read one key row with 16-byte
+// loads.  Each wave keeps a running best-64 list across lanes, merging every
+// scored batch with a 64-lane bitonic network (sort the batch, take the
+// element-wise better of the running list and the reversed batch, then a
+// bitonic merge).  The four waves' lists meet in LDS and wave 0 merges them.
+#include <float.h>
+#include <limits.h>
+
+#include "gsa_internal.h"
+
+namespace gsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline bool better(float s1, int i1, float s2, int i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// One compare-exchange stage of a 64-lane bitonic network: the lane keeps the
+// better of (own, partner at lane ^ j) if keep_better, else the worse.
+__device__ inline void cx(float& s, int& id, int j, bool keep_better) {
+  const float os = __shfl_xor(s, j);
+  const int oi = __shfl_xor(id, j);
+  if (better(os, oi, s, id) == keep_better) {
+    s = os;
+    id = oi;
+  }
+}
+
+// Sort 64 (score, id) pairs across the wave, best first.
+__device__ inline void wave_sort_best_first(float& s, int& id) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const bool up = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      cx(s, id, j, lower == up);
+    }
+  }
+}
+
+// Running best-first list (rs, ri) absorbs another best-first list (xs, xi).
+__device__ inline void wave_merge(float& rs, int& ri, float xs, int xi) {
+  const int lane = __lane_id();
+  const float ys = __shfl(xs, 63 - lane);
+  const int yi = __shfl(xi, 63 - lane);
+  if (better(ys, yi, rs, ri)) {
+    rs = ys;
+    ri = yi;
+  }
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) cx(rs, ri, j, (lane & j) == 0);
+}
+
+__device__ inline void wave_sort_int_asc(int& v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = __shfl_xor(v, j);
+      const bool up = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      const bool keep_small = lower == up;
+      if ((o < v) == keep_small && o != v) v = o;
+    }
+  }
+}
+
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int n = 4;
+  __device__ static void load(const float* p, float* out) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[3];
+  }
+  __device__ static float one(const float* p) { return *p; }
+};
+template <> struct Vec16<unsigned short> {
+  static constexpr int n = 8;
+  __device__ static void load(const unsigned short* p, float* out) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[2 * j] = lo_bf16(w[j]);
+      out[2 * j + 1] = hi_bf16(w[j]);
+    }
+  }
+  __device__ static float one(const unsigned short* p) { return bf16_to_f32(*p); }
+};
+
+// Candidate -> gist positions / id, for the three kinds of candidate.
+struct ChunkCands {        // single level: chunk e, gists pos_of(GIST, e*g + t)
+  const Lay* l;
+  __device__ int ngist() const { return l->g; }
+  __device__ int pos(int e, int t) const { return pos_of(*l, K_GIST, e * l->g + t); }
+  __device__ int id(int e) const { return e; }
+};
+struct GroupCands {        // two levels, level 2: group e
+  const Lay* l;
+  __device__ int ngist() const { return l->g2; }
+  __device__ int pos(int e, int t) const { return pos_of(*l, K_GIST2, e * l->g2 + t); }
+  __device__ int id(int e) const { return e; }
+};
+struct InGroupCands {      // two levels, level 1: chunks of the kept groups
+  const Lay* l;
+  const int* groups;       // LDS, ascending
+  __device__ int chunk(int e) const { return groups[e / l->G2] * l->G2 + e % l->G2; }
+  __device__ int ngist() const { return l->g; }
+  __device__ int pos(int e, int t) const { return pos_of(*l, K_GIST, chunk(e) * l->g + t); }
+  __device__ int id(int e) const { return chunk(e); }
+};
+
+// Score `ncand` candidates and leave the wave-merged best-64 list in lanes of
+// wave 0 (rs, ri); every wave returns after the block-wide merge.
+template <typename T, int D, typename Cands>
+__device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const float* __restrict__ qbar,
+                               int ncand, float mul, const Cands& cands, float* __restrict__ score_out,
+                               float* lds_s, int* lds_i, float& rs, int& ri) {
+  using V = Vec16<T>;
+  constexpr int EPL = V::n;          // elements per 16-byte load
+  constexpr int LPR = D / EPL;       // lanes per key row
+  constexpr int RPI = 64 / LPR;      // key rows per wave instruction
+  constexpr int ITER = LPR;          // instructions per batch of 64 rows
+  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  const int sub = lane % LPR, grp = lane / LPR;
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qbar[sub * EPL + e];
+
+  rs = -FLT_MAX;
+  ri = INT_MAX;
+  rs = -__builtin_inff();
+  const int nbatch = (ncand + 63) / 64;
+  const int ng = cands.ngist();
+  for (int bi = wave; bi < nbatch; bi += kWaves) {
+    float part[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int e = bi * 64 + grp + RPI * it;
+      float acc = 0.f;
+      if (e < ncand) {
+        for (int t = 0; t < ng; ++t) {
+          float kv[EPL];
+          V::load(kb + (int64_t)cands.pos(e, t) * kst + sub * EPL, kv);
+#pragma unroll
+          for (int x = 0; x < EPL; ++x) acc = fmaf(qv[x], kv[x], acc);
+        }
+      }
+      part[it] = acc;
+    }
+    float mine = 0.f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      float v = part[it];
+#pragma unroll
+      for (int j = 1; j < LPR; j <<= 1) v += __shfl_xor(v, j);
+      if (sub == it) mine = v;
+    }
+    const int e = bi * 64 + grp + RPI * sub;
+    float s = -__builtin_inff();
+    int id = INT_MAX;
+    if (e < ncand) {
+      s = mine * mul;
+      id = cands.id(e);
+      if (score_out) score_out[id] = s;
+    }
+    wave_sort_best_first(s, id);
+    wave_merge(rs, ri, s, id);
+  }
+  lds_s[wave * 64 + lane] = rs;
+  lds_i[wave * 64 + lane] = ri;
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < kWaves; ++w) wave_merge(rs, ri, lds_s[w * 64 + lane], lds_i[w * 64 + lane]);
+  }
+  __syncthreads();
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void k_score_select(
+    Lay l, const T* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh, const T* __restrict__ k,
+    int64_t ksb, int64_t kst, int64_t ksh, int Hq, int Hkv, int q_begin, int q_len, float scale,
+    int* __restrict__ sel, int* __restrict__ selg, float* __restrict__ scores, int ncols) {
+  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = Hq / Hkv;
+  const int i = q_begin + r;
+  __shared__ float qbar[D];
+  __shared__ float lds_s[kWaves * 64];
+  __shared__ int lds_i[kWaves * 64];
+  __shared__ int kept[64];
+
+  for (int e = tid; e < D; e += kThreads) {
+    float s = 0.f;
+    for (int g = 0; g < G; ++g) s += Vec16<T>::one(q + b * qsb + r * qst + (int64_t)(h * G + g) * qsh + e);
+    qbar[e] = s / (float)G;
+  }
+  __syncthreads();
+  const T* kb = k + b * ksb + h * ksh;
+  const size_t row = ((size_t)b * Hkv + h) * q_len + r;
+  float rs;
+  int ri;
+
+  if (l.G2 == 0) {
+    const int ncand = i >= l.S ? (i - l.S) / l.P : 0;
+    float* so = scores ? scores + row * ncols : nullptr;
+    if (so)
+      for (int e = ncand + tid; e < ncols; e += kThreads) so[e] = -__builtin_inff();
+    ChunkCands cands{&l};
+    score_and_rank<T, D>(kb, kst, qbar, ncand, scale / (float)l.g, cands, so, lds_s, lds_i, rs, ri);
+    if (wave == 0) {
+      int v = (lane < l.k && ri != INT_MAX) ? ri : INT_MAX;
+      wave_sort_int_asc(v);
+      if (lane < l.k) sel[row * l.k + lane] = v == INT_MAX ? -1 : v;
+    }
+    return;
+  }
+
+  // level 2: groups whose level-2 gists all precede the query
+  const int ng2 = i >= l.S ? (i - l.S) / l.P2 : 0;
+  float* so = scores ? scores + row * ncols : nullptr;
+  if (so)
+    for (int e = ng2 + tid; e < ncols; e += kThreads) so[e] = -__builtin_inff();
+  GroupCands gc{&l};
+  score_and_rank<T, D>(kb, kst, qbar, ng2, scale / (float)l.g2, gc, so, lds_s, lds_i, rs, ri);
+  __shared__ int nkept;
+  if (wave == 0) {
+    int v = (lane < l.k2 && ri != INT_MAX) ? ri : INT_MAX;
+    wave_sort_int_asc(v);
+    if (lane < l.k2) selg[row * l.k2 + lane] = v == INT_MAX ? -1 : v;
+    kept[lane] = v;
+    const unsigned long long bal = __ballot(v != INT_MAX);
+    if (lane == 0) nkept = __popcll(bal);
+  }
+  __syncthreads();
+  // level 1: chunks of the kept groups
+  InGroupCands ic{&l, kept};
+  score_and_rank<T, D>(kb, kst, qbar, nkept * l.G2, scale / (float)l.g, ic, nullptr, lds_s, lds_i, rs, ri);
+  if (wave == 0) {
+    int v = (lane < l.k && ri != INT_MAX) ? ri : INT_MAX;
+    wave_sort_int_asc(v);
+    if (lane < l.k) sel[row * l.k + lane] = v == INT_MAX ? -1 : v;
+  }
+}
+
+template <typename T, int D>
+void launch(const Lay& l, const gsa_tensor& q, const gsa_tensor& k, int B, int Hq, int Hkv, int q_begin,
+            int q_len, float scale, int* sel, int* selg, float* scores, int ncols, hipStream_t st) {
+  hipLaunchKernelGGL((k_score_select<T, D>), dim3(q_len, Hkv, B), dim3(kThreads), 0, st, l,
+                     (const T*)q.ptr, q.stride_b, q.stride_t, q.stride_h, (const T*)k.ptr, k.stride_b,
+                     k.stride_t, k.stride_h, Hq, Hkv, q_begin, q_len, scale, sel, selg, scores, ncols);
+}
+
+}  // namespace
+}  // namespace gsa
+
+using namespace gsa;
+
+extern "C" gsa_status gsa_score_select(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, int32_t B,
+                                       int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                                       int32_t q_begin, int32_t q_len, float scale, int32_t* sel,
+                                       int32_t* sel_groups, float* scores, void* stream) {
+  Lay l;
+  gsa_status st = make_lay(layout, seq_len, 64, &l);
+  if (st != GSA_OK) return st;
+  if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
+  if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
+  if (q.dtype != k.dtype) return fail(GSA_EINVAL, "q and k dtypes differ");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(GSA_EINVAL, "bad head counts B=%d Hq=%d Hkv=%d", B, Hq, Hkv);
+  if (d != 64 && d != 128) return fail(GSA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (l.k < 1 || l.k > 64) return fail(GSA_EUNSUPPORTED, "top_k %d outside [1, 64]", l.k);
+  if (l.G2 > 0 && l.k2 > 64) return fail(GSA_EUNSUPPORTED, "l2_top_k %d > 64", l.k2);
+  if (l.G2 > 0 && l.k2 * l.G2 > 1 << 20) return fail(GSA_EUNSUPPORTED, "l2_top_k * l2_chunks too large");
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (!sel) return fail(GSA_EINVAL, "sel is NULL");
+  if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is NULL with two levels");
+  if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
+  if (q_len == 0) return GSA_OK;
+  const int ncols = gsa_score_columns(layout, seq_len);
+  hipStream_t s = (hipStream_t)stream;
+  if (q.dtype == GSA_F32) {
+    if (d == 64) launch<float, 64>(l, q, k, B, Hq, Hkv, q_begin, q_len, scale, sel, sel_groups, scores, ncols, s);
+    else launch<float, 128>(l, q, k, B, Hq, Hkv, q_begin, q_len, scale, sel, sel_groups, scores, ncols, s);
+  } else {
+    if (d == 64) launch<unsigned short, 64>(l, q, k, B, Hq, Hkv, q_begin, q_len, scale, sel, sel_groups, scores, ncols, s);
+    else launch<unsigned short, 128>(l, q, k, B, Hq, Hkv, q_begin, q_len, scale, sel, sel_groups, scores, ncols, s);
+  }
+  return launch_status("gsa_score_select");
+}

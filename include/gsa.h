@@ -1,0 +1,182 @@
+/*
+ * gsa.h -- C ABI of the gist-token sparse attention library (libgsa.so, gfx950).
+ *
+ * The method.  A sequence is laid out as n_sink sink tokens, then chunks of
+ * chunk_len raw tokens each followed by gists_per_chunk gist tokens (fine,
+ * interleaved gists: "A Silver Bullet or a Compromise for Full Attention?",
+ * §2 Preliminaries; compression ratio = chunk_len / gists_per_chunk).  A query
+ * attends to the sinks, every earlier gist, a causal local window and itself
+ * (UniGist summary, Approach), plus the raw tokens of the top_k chunks whose
+ * gist keys score highest against it (selective unfolding: Simplified Sparse
+ * Attention via Gist Tokens, abstract; Forget, Then Recall ... Gist Sparse
+ * Attention, abstract).  top_k = 0 is the fixed sink/gist/window layout.  With
+ * l2_chunks > 0 a second level groups l2_chunks chunks followed by l2_gists
+ * level-2 gists (gist of gist, same two abstracts): the query scores the
+ * groups by their level-2 gists, keeps l2_top_k, scores the chunks of those
+ * groups by their level-1 gists and unfolds top_k of them; it sees every
+ * level-2 gist, the level-1 gists of the kept groups, the window and the
+ * unfolded raw tokens.
+ *
+ * Readings fixed by this library where the pages are silent: the window W
+ * counts interleaved positions and includes the query itself (key j visible
+ * iff 0 <= i - j < max(W, 1)); a chunk is a candidate once all its gists are
+ * earlier than the query; a chunk's score for one KV head is the mean, over
+ * that KV group's query heads (and over the chunk's gists), of q.k*scale; ties
+ * go to the lower chunk index.  Q and K arrive after any position encoding.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory and keeps no device state between calls.
+ *   - Work is only enqueued on `stream` (a hipStream_t; NULL = null stream);
+ *     no call synchronises.  Faults inside kernels surface at the caller's
+ *     next synchronisation.
+ *   - Every argument is checked before anything is enqueued: GSA_EINVAL means
+ *     nothing was launched; gsa_last_error() gives the reason (thread-local).
+ *   - Integer index outputs are int32, ascending, padded with -1.
+ *   - Tensors are described by gsa_tensor: element strides for batch, token
+ *     position and head; the head dimension d is contiguous.  Pointers must be
+ *     16-byte aligned and strides multiples of 16 bytes.
+ */
+#ifndef GSA_H
+#define GSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GSA_OK = 0,
+  GSA_EINVAL = 1,        /* bad argument; nothing enqueued */
+  GSA_EUNSUPPORTED = 2,  /* valid but not implemented (head dim, dtype, size) */
+  GSA_EHIP = 3           /* the HIP runtime refused a launch */
+} gsa_status;
+
+typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype;
+
+typedef struct {
+  int32_t n_sink;          /* sink tokens at positions [0, n_sink) */
+  int32_t chunk_len;       /* c: raw tokens per (level-1) chunk, >= 1 */
+  int32_t gists_per_chunk; /* g: gist tokens after each chunk, >= 1 */
+  int32_t window;          /* W: local window in positions, self included */
+  int32_t top_k;           /* chunks unfolded per query; 0 = fixed layout */
+  int32_t l2_chunks;       /* chunks per level-2 group; 0 = single level */
+  int32_t l2_gists;        /* level-2 gists after each group */
+  int32_t l2_top_k;        /* groups kept per query (two levels) */
+} gsa_layout;
+
+typedef struct {
+  void* ptr;               /* device pointer to element [0,0,0,0] */
+  int32_t dtype;           /* gsa_dtype */
+  int32_t reserved;        /* must be 0 */
+  int64_t stride_b;        /* elements between batches */
+  int64_t stride_t;        /* elements between token positions */
+  int64_t stride_h;        /* elements between heads */
+} gsa_tensor;
+
+/* Stream-ordered key tiles.  Key columns of the visibility table are the
+ * sequence's positions regrouped by stream -- sinks | level-2 gists | gists |
+ * raws, ascending inside each stream -- and each stream is cut into tiles of
+ * block_n columns (the last tile of a stream may be short; no tile spans two
+ * streams).  Rows are query positions [q_begin, q_begin + q_len) cut into
+ * tiles of block_m rows.  A tile is coded 0 (no visible pair), 1 (some) or
+ * 2 (all).  Grouping the gists into one stream is what lets the prefill skip
+ * whole invisible tiles, the purpose UniGist's summary gives for moving its
+ * gists (Approach). */
+
+/* Host only.  Table dimensions for a sequence of seq_len positions. */
+gsa_status gsa_table_dims(const gsa_layout* layout, int32_t seq_len, int32_t q_len,
+                          int32_t block_m, int32_t block_n, int32_t* n_q_tiles,
+                          int32_t* n_k_tiles);
+
+/* Block-visibility table (UniGist summary, Approach; SSA abstract for the
+ * unfolded chunks).
+ *   seq_len       positions of the sequence (keys are [0, seq_len))
+ *   q_begin,q_len query rows; q_begin + q_len <= seq_len
+ *   sel           NULL iff top_k == 0 and single level; else int32
+ *                 [n_tables, q_len, top_k] (the gsa_score_select output of one
+ *                 (batch, KV head) per table)
+ *   sel_groups    two levels: int32 [n_tables, q_len, l2_top_k]; else NULL
+ *   n_tables      1 for the fixed layout, else batch * KV heads
+ *   table         int8  [n_tables, n_q_tiles, n_k_tiles]   (out)
+ *   tile_cnt      int32 [n_tables, n_q_tiles]              (out) non-empty tiles per row
+ *   tile_list     int32 [n_tables, n_q_tiles, n_k_tiles]   (out) their ids, ascending,
+ *                 row-padded (entries past tile_cnt are left untouched) */
+gsa_status gsa_build_layout(const gsa_layout* layout, int32_t seq_len, int32_t q_begin,
+                            int32_t q_len, int32_t block_m, int32_t block_n,
+                            const int32_t* sel, const int32_t* sel_groups, int32_t n_tables,
+                            int8_t* table, int32_t* tile_cnt, int32_t* tile_list, void* stream);
+
+/* Gist scoring and per-KV-group top-k (SSA abstract: score chunks against the
+ * gist keys only, keep the top k; GSA abstract: two levels).
+ *   q        [B, q_len, Hq, d] (row r is the query at position q_begin + r)
+ *   k        keys of the whole sequence, [B, seq_len, Hkv, d] by strides (a
+ *            [B, Hkv, seq_len, d] cache works the same way)
+ *   scale    logit scale, normally 1/sqrt(d)
+ *   sel      int32 [B, Hkv, q_len, top_k] (out)
+ *   sel_groups two levels: int32 [B, Hkv, q_len, l2_top_k] (out); else NULL
+ *   scores   nullable float [B, Hkv, q_len, n_cand]: the score of every candidate
+ *            of the first level (chunks; groups with two levels), -inf where not
+ *            yet a candidate; n_cand = gsa_score_columns().
+ * Requires 1 <= top_k <= 64, l2_top_k <= 64, d in {64, 128}. */
+gsa_status gsa_score_select(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                            int32_t q_begin, int32_t q_len, float scale, int32_t* sel,
+                            int32_t* sel_groups, float* scores, void* stream);
+
+/* Host only.  Columns of the optional scores output of gsa_score_select. */
+int32_t gsa_score_columns(const gsa_layout* layout, int32_t seq_len);
+
+/* Block-sparse prefill: softmax attention of every query row over its visible
+ * keys, skipping EMPTY tiles and masking only PARTIAL ones.
+ *   q, o     [B, q_len, Hq, d]; k, v [B, seq_len, Hkv, d] (by strides)
+ *   o        dtype F32, or the input dtype
+ *   lse      nullable float [B, Hq, q_len], natural-log log-sum-exp
+ *   sel, sel_groups  as produced by gsa_score_select (NULL for the fixed layout)
+ *   table, tile_cnt, tile_list  from gsa_build_layout with the same block_m,
+ *            block_n, q_begin, q_len (n_tables = 1 for the fixed layout, else B*Hkv)
+ * bf16 with d in {64,128} runs on MFMA and needs block_m, block_n from
+ * gsa_prefill_tile(); f32 accepts any block_m and block_n <= 256. */
+gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                            gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                            const int32_t* sel, const int32_t* sel_groups, const int8_t* table,
+                            const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m,
+                            int32_t block_n, float scale, void* stream);
+
+/* Host only.  Tile shape the prefill kernel for (dtype, d) expects. */
+gsa_status gsa_prefill_tile(int32_t dtype, int32_t d, int32_t* block_m, int32_t* block_n);
+
+/* Split-K decode: one query per sequence at position kv_len - 1 (the caller has
+ * already appended that token's K and V to the cache), attending to the sinks,
+ * every gist earlier than the window (two levels: every level-2 gist and the
+ * level-1 gists of the kept groups), the window and the unfolded chunks.
+ *   q, o     [B, Hq, d] (stride_t unused)
+ *   k_cache, v_cache  [B, Hkv, kv_len, d] (by strides), bf16
+ *   lse      nullable float [B, Hq]
+ *   sel      int32 [B, Hkv, 1, top_k]; sel_groups [B, Hkv, 1, l2_top_k] or NULL
+ *   ws       device workspace of at least gsa_decode_workspace_bytes(); its
+ *            contents need no initialisation and are clobbered.
+ * Requires bf16 inputs, d in {64,128}, Hq/Hkv <= 16. */
+gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
+                           gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
+                           int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
+                           const int32_t* sel_groups, float scale, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Host only.  Workspace bytes gsa_attn_decode needs for these sizes. */
+size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
+                                  int32_t d, int32_t kv_len);
+
+const char* gsa_status_str(gsa_status status);
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char* gsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSA_H */
