@@ -129,7 +129,7 @@ def cpu_baseline(w, q, k, v, rows_per_head: int):
         with ctx.Pool(workers) as pool:
             pool.map(_oracle_worker, range(w.hkv))
         dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"{len(rows)} query rows spread over the 41088 positions x all {w.hq} heads "
                       f"(batch {w.batch}), fp64 numpy, {workers} processes x 1 BLAS thread, "
                       f"{dt:.1f} s wall"}
@@ -231,9 +231,11 @@ def run_decode(w, args, torch, gsa, copies=4):
                 starts = [S + (m // G2) * P2 + (m % G2) * P for m in sl[bb, h, 0] if m >= 0]
             rows += min(S, lo) + n_g + (i - lo + 1) + sum(min(max(lo - s0, 0), c) for s0 in starts)
     nbytes = rows * 2 * w.d * 2 + w.batch * w.hq * w.d * 2 * 2 + sl.nbytes + (0 if sg is None else sg.nbytes)
-    return {"workload": w.name, "ms_per_step": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9,
-            "unique_bytes": nbytes, "visible_rows_per_group": rows / (w.batch * w.hkv),
-            "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    nbytes = int(nbytes)
+    return {"workload": w.name, "ms_per_step": round(ms, 5),
+            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "unique_bytes": nbytes,
+            "visible_rows_per_group": round(float(rows) / (w.batch * w.hkv), 2),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernels": "score_select + decode_split + decode_combine", "cache_copies": copies}
 
 
@@ -265,7 +267,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=640)
+    ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
