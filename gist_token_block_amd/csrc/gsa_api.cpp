@@ -44,6 +44,9 @@ gsa_status make_lay(const gsa_layout* p, int L, int bn, Lay* out) {
     return fail(GSA_EINVAL, "l2_gists / l2_top_k set without l2_chunks");
   }
   if (L < 0) return fail(GSA_EINVAL, "sequence length %d < 0", L);
+  if (p->chunk_len > (1 << 20) || p->gists_per_chunk > (1 << 20) || p->l2_chunks > (1 << 16) ||
+      p->l2_gists > (1 << 20))
+    return fail(GSA_EUNSUPPORTED, "layout periods too large");
   if (bn < 1) return fail(GSA_EINVAL, "block_n %d < 1", bn);
   Lay l{};
   l.S = p->n_sink;
@@ -59,6 +62,12 @@ gsa_status make_lay(const gsa_layout* p, int L, int bn, Lay* out) {
   l.P2 = l.GP + l.g2;
   l.L = L;
   l.bn = bn;
+  l.dc = make_fdiv(l.c);
+  l.dg = make_fdiv(l.g);
+  l.dP = make_fdiv(l.P);
+  l.dG2 = make_fdiv(l.G2 > 0 ? l.G2 : 1);
+  l.dg2 = make_fdiv(l.g2 > 0 ? l.g2 : 1);
+  l.dP2 = make_fdiv(l.P2 > 0 ? l.P2 : 1);
   if (l.G2 == 0) {
     l.nstr = 3;
     l.kind[0] = K_SINK; l.kind[1] = K_GIST; l.kind[2] = K_RAW;
@@ -66,12 +75,30 @@ gsa_status make_lay(const gsa_layout* p, int L, int bn, Lay* out) {
     l.nstr = 4;
     l.kind[0] = K_SINK; l.kind[1] = K_GIST2; l.kind[2] = K_GIST; l.kind[3] = K_RAW;
   }
+  for (int s = 0; s < l.nstr; ++s) {
+    StreamMap m{};
+    m.per = 1; m.G = 1 << 30; m.stride1 = 1; m.stride2 = 0; m.base = 0;
+    switch (l.kind[s]) {
+      case K_SINK: break;
+      case K_GIST2: m.per = l.g2; m.stride1 = l.P2; m.base = l.S + l.GP; break;
+      case K_GIST:
+        m.per = l.g; m.stride1 = l.P; m.base = l.S + l.c;
+        if (l.G2) { m.G = l.G2; m.stride2 = l.P2; }
+        break;
+      case K_RAW:
+        m.per = l.c; m.stride1 = l.P; m.base = l.S;
+        if (l.G2) { m.G = l.G2; m.stride2 = l.P2; }
+        break;
+    }
+    m.dper = make_fdiv(m.per);
+    m.dG = make_fdiv(m.G);
+    l.smap[s] = m;
+  }
   int t0 = 0;
   for (int s = 0; s < l.nstr; ++s) {
     l.len[s] = count_below(l, l.kind[s], L);
-    l.ntile[s] = (l.len[s] + bn - 1) / bn;
     l.tile0[s] = t0;
-    t0 += l.ntile[s];
+    t0 += (l.len[s] + bn - 1) / bn;
   }
   l.nkt = t0;
   *out = l;

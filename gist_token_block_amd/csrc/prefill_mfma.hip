@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
     const int* __restrict__ tile_list, float c2, int fixed, int total) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short Klds[kBN * C::KP];
-  __shared__ __attribute__((aligned(16))) unsigned short VTlds[D * C::VTP];
+  __shared__ __attribute__((aligned(16))) unsigned short Klds[2 * kBN * C::KP];     // double buffered
+  __shared__ __attribute__((aligned(16))) unsigned short VTlds[2 * D * C::VTP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -122,62 +122,93 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
 
-  for (int idx = 0; idx < cnt; ++idx) {
-    const int kt = list[idx];
-    const int code = codes[kt];
-    int kind, u0, u1;
-    tile_span(l, kt, kind, u0, u1);
-    const int width = u1 - u0;
+  // Staging roles.  K: key rows tid / PPR + RPP * it, 16-byte piece tid % PPR.
+  // V: keys 4 rg .. 4 rg + 3 of d-piece pc, written transposed.
+  constexpr int RPP = kThreads / C::PPR;
+  constexpr int NKL = kBN / RPP;              // K loads per thread
+  const int kpiece = tid % C::PPR, krow0 = tid / C::PPR;
+  const bool vrole = tid < 16 * C::PPR;
+  const int rg = tid & 15, pc = tid >> 4;
+  u32x4 kreg[NKL], vreg[4];
 
-    // ---- stage K (row-major) and V (transposed) into LDS
-    {
-      constexpr int RPP = kThreads / C::PPR;  // key rows per pass
+  // Fetch tile `idx` of the row's list into kreg / vreg (zeros past the tile).
+  // Rows past a short tile re-read its last row: those keys are masked to
+  // -inf, so their P is 0 and the duplicate (finite) values never count.
+  auto fetch = [&](int idx, int& slot, int& kind, int& u0, int& width, int& code) {
+    const int kt = list[idx];
+    code = codes[kt];
+    int u1;
+    slot = tile_span(l, kt, kind, u0, u1);
+    width = u1 - u0;
+    const StreamMap sm = l.smap[slot];
+    if (sm.per == 1 && sm.G == (1 << 30)) {
+      // affine stream (sinks; gists when g == 1): position = base + u * stride1
+      const int p0 = sm.base + u0 * sm.stride1;
+      const unsigned short* k0 = kb + (int64_t)p0 * kst + kpiece * 8;
+      const unsigned short* v0 = vb + (int64_t)p0 * vst + pc * 8;
+      const int64_t kstep = (int64_t)sm.stride1 * kst, vstep = (int64_t)sm.stride1 * vst;
 #pragma unroll
-      for (int it = 0; it < kBN / RPP; ++it) {
-        const int key = tid / C::PPR + RPP * it;
-        const int piece = tid % C::PPR;
-        u32x4 w = u32x4{0u, 0u, 0u, 0u};
-        if (key < width) {
-          const int p = pos_of(l, kind, u0 + key);
-          w = *reinterpret_cast<const u32x4*>(kb + (int64_t)p * kst + piece * 8);
-        }
-        *reinterpret_cast<u32x4*>(&Klds[key * C::KP + piece * 8]) = w;
+      for (int it = 0; it < NKL; ++it)
+        kreg[it] = *reinterpret_cast<const u32x4*>(k0 + imin(krow0 + RPP * it, width - 1) * kstep);
+      if (vrole) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          vreg[a] = *reinterpret_cast<const u32x4*>(v0 + imin(4 * rg + a, width - 1) * vstep);
       }
-      if (tid < 16 * C::PPR) {
-        const int rg = tid & 15, pc = tid >> 4;
-        u32x4 w[4];
+      return;
+    }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int key = 4 * rg + a;
-          w[a] = u32x4{0u, 0u, 0u, 0u};
-          if (key < width) {
-            const int p = pos_of(l, kind, u0 + key);
-            w[a] = *reinterpret_cast<const u32x4*>(vb + (int64_t)p * vst + pc * 8);
-          }
-        }
+    for (int it = 0; it < NKL; ++it) {
+      const int key = imin(krow0 + RPP * it, width - 1);
+      kreg[it] = *reinterpret_cast<const u32x4*>(kb + (int64_t)map_pos(sm, u0 + key) * kst + kpiece * 8);
+    }
+    if (vrole) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dw = e >> 1;
-          unsigned lo, hi;
-          if (e & 1) {
-            lo = (w[0][dw] >> 16) | (w[1][dw] & 0xffff0000u);
-            hi = (w[2][dw] >> 16) | (w[3][dw] & 0xffff0000u);
-          } else {
-            lo = (w[0][dw] & 0xffffu) | (w[1][dw] << 16);
-            hi = (w[2][dw] & 0xffffu) | (w[3][dw] << 16);
-          }
-          *reinterpret_cast<u32x2*>(&VTlds[(pc * 8 + e) * C::VTP + 4 * rg]) = u32x2{lo, hi};
-        }
+      for (int a = 0; a < 4; ++a) {
+        const int key = imin(4 * rg + a, width - 1);
+        vreg[a] = *reinterpret_cast<const u32x4*>(vb + (int64_t)map_pos(sm, u0 + key) * vst + pc * 8);
       }
     }
+  };
+
+  int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0;
+  if (cnt > 0) fetch(0, nslot, nkind, nu0, nwidth, ncode);
+
+  for (int idx = 0; idx < cnt; ++idx) {
+    const int slot = nslot, kind = nkind, u0 = nu0, width = nwidth, code = ncode;
+    unsigned short* Kb = Klds + (idx & 1) * (kBN * C::KP);
+    unsigned short* VTb = VTlds + (idx & 1) * (D * C::VTP);
+
+    // ---- registers -> LDS (K row-major, V transposed: 4 keys per 8-byte write)
+#pragma unroll
+    for (int it = 0; it < NKL; ++it)
+      *reinterpret_cast<u32x4*>(&Kb[(krow0 + RPP * it) * C::KP + kpiece * 8]) = kreg[it];
+    if (vrole) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dw = e >> 1;
+        unsigned lo, hi;
+        if (e & 1) {
+          lo = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
+          hi = (vreg[2][dw] >> 16) | (vreg[3][dw] & 0xffff0000u);
+        } else {
+          lo = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
+          hi = (vreg[2][dw] & 0xffffu) | (vreg[3][dw] << 16);
+        }
+        *reinterpret_cast<u32x2*>(&VTb[(pc * 8 + e) * C::VTP + 4 * rg]) = u32x2{lo, hi};
+      }
+    }
+    // One barrier per tile: it publishes this tile's buffer, and every wave
+    // has finished the tile before last, whose buffer the next write reuses.
     __syncthreads();
+    if (idx + 1 < cnt) fetch(idx + 1, nslot, nkind, nu0, nwidth, ncode);
 
     // ---- S^T = K Q^T : two 32x32 tiles (keys 0..31, 32..63) x this wave's 32 queries
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Klds[n * C::KP + 8 * h2 + 16 * ks]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Klds[(32 + n) * C::KP + 8 * h2 + 16 * ks]);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Kb[n * C::KP + 8 * h2 + 16 * ks]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Kb[(32 + n) * C::KP + 8 * h2 + 16 * ks]);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
     }
@@ -190,8 +221,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
         const int key1 = key0 + 32;
         bool v0 = key0 < width, v1 = key1 < width;
         if (code != 2) {
-          if (v0) v0 = key_visible(l, i, kind, u0 + key0, pos_of(l, kind, u0 + key0), selrow, selgrow);
-          if (v1) v1 = key_visible(l, i, kind, u0 + key1, pos_of(l, kind, u0 + key1), selrow, selgrow);
+          if (v0) v0 = key_visible(l, i, kind, u0 + key0, map_pos(l.smap[slot], u0 + key0), selrow, selgrow);
+          if (v1) v1 = key_visible(l, i, kind, u0 + key1, map_pos(l.smap[slot], u0 + key1), selrow, selgrow);
         }
         if (!v0) s0[j] = -__builtin_inff();
         if (!v1) s1[j] = -__builtin_inff();
@@ -204,7 +235,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__ballot(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
+    }
+    m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -212,10 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       s1[j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -m_new));
       psum += s0[j] + s1[j];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
+    l_run += psum;
 
     // P^T operands: step st uses tile st/2, accumulator regs 8(st%2)..+7
     bf16x8 pk[4];
@@ -234,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     // ---- O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      const unsigned short* vrow = &VTlds[(32 * mt + n) * C::VTP];
+      const unsigned short* vrow = &VTb[(32 * mt + n) * C::VTP];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * st + 4 * h2);
@@ -244,7 +278,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
                                                            oacc[mt], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   // ---- normalise and store: lane holds O^T[d][query n], d = 32mt + 8(j/4) + 4h2 + j%4
