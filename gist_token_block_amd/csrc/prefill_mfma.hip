@@ -11,15 +11,19 @@
 //
 // Workgroup: 4 waves, 128 query rows of one query head; wave w owns rows
 // [32w, 32w+32).  Per key tile:
-//   * K tile [64 keys][d] staged to LDS row-major; V tile staged transposed
-//     [d][64 keys] so the PV operand reads are contiguous in keys.
+//   * K and V tiles [64 keys][d] go straight from HBM/L2 into LDS with
+//     global_load_lds_dwordx4 (no staging registers), double buffered: the
+//     next tile streams in while this one is computed.  16-byte pieces are
+//     XOR-swizzled per row so both read patterns below are bank-conflict free.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so
 //     a lane's 32 logits belong to one query: the row max and sum are in-lane
 //     plus one exchange between the two lane halves.
 //   * Online softmax in base 2 (scale * log2 e folded into one FMA).
-//   * O^T += V^T P^T with the same MFMA; P goes from the S accumulators to
-//     bf16 operands without leaving registers: the k-index of both operands is
-//     mapped to the key each lane already holds.
+//   * O^T += V^T P^T with the same MFMA.  The V^T operand is read from the
+//     row-major V tile with ds_read_b64_tr_b16 (each 16-lane group gathers a
+//     4-key x 16-d block and hands every lane one d with 4 keys); P goes from
+//     the S accumulators to bf16 operands without leaving registers, the
+//     k-index of both operands mapped to the key each lane already holds.
 // Work order: blockIdx is remapped so that each XCD (blockIdx % 8) runs a
 // contiguous range of (batch, KV head, query tile descending, query head):
 // the query heads sharing a KV head and the neighbouring query tiles, which
@@ -42,12 +46,19 @@ constexpr int kBN = 64;
 constexpr int kThreads = 256;
 
 template <int D> struct Cfg {
-  static constexpr int KP = D + 8;       // K tile pitch (elements), rows 16-byte aligned
-  static constexpr int VTP = kBN + 4;    // V^T tile pitch (elements), rows 8-byte aligned
+  static constexpr int PPR = D / 8;      // 16-byte pieces per key row
+  static constexpr int RPI = 64 / PPR;   // key rows per 1 KB wave load
+  static constexpr int NIW = kBN / RPI / 4;  // wave loads per tile per wave (K, and again V)
   static constexpr int KS = D / 16;      // k-steps of the QK product
   static constexpr int MT = D / 32;      // 32-row output tiles of O^T
-  static constexpr int PPR = D / 8;      // 16-byte pieces per key row
 };
+// 16-byte piece p of key row r sits at slot p ^ swz(r).
+template <int D> __device__ inline int swz_k(int r) { return r & (D / 8 - 1); }
+__device__ inline int swz_v(int r) { return 2 * (r & 3); }
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* glb_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 template <typename TO> struct OutStore;
 template <> struct OutStore<float> {
@@ -71,8 +82,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
     const int* __restrict__ tile_list, float c2, int fixed, int total) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short Klds[2 * kBN * C::KP];     // double buffered
-  __shared__ __attribute__((aligned(16))) unsigned short VTlds[2 * D * C::VTP];
+  __shared__ __attribute__((aligned(1024))) unsigned short Klds[2 * kBN * D];   // double buffered
+  __shared__ __attribute__((aligned(1024))) unsigned short Vlds[2 * kBN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -122,93 +133,61 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
 
-  // Staging roles.  K: key rows tid / PPR + RPP * it, 16-byte piece tid % PPR.
-  // V: keys 4 rg .. 4 rg + 3 of d-piece pc, written transposed.
-  constexpr int RPP = kThreads / C::PPR;
-  constexpr int NKL = kBN / RPP;              // K loads per thread
-  const int kpiece = tid % C::PPR, krow0 = tid / C::PPR;
-  const bool vrole = tid < 16 * C::PPR;
-  const int rg = tid & 15, pc = tid >> 4;
-  u32x4 kreg[NKL], vreg[4];
-
-  // Fetch tile `idx` of the row's list into kreg / vreg (zeros past the tile).
-  // Rows past a short tile re-read its last row: those keys are masked to
-  // -inf, so their P is 0 and the duplicate (finite) values never count.
-  auto fetch = [&](int idx, int& slot, int& kind, int& u0, int& width, int& code) {
+  // Staging: wave load `wi` (0 .. 4*NIW-1) fills key rows [wi*RPI, wi*RPI+RPI)
+  // of a tile; lane -> row wi*RPI + lane / PPR, LDS slot lane % PPR, which
+  // holds the row's 16-byte piece slot ^ swz(row).  Rows past a short tile
+  // re-read its last row: those keys are masked to -inf, so their P is 0 and
+  // the duplicate (finite) values never count.
+  const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  auto fetch = [&](int idx, int buf, int& slot, int& kind, int& u0, int& width, int& code) {
     const int kt = list[idx];
     code = codes[kt];
     int u1;
     slot = tile_span(l, kt, kind, u0, u1);
     width = u1 - u0;
     const StreamMap sm = l.smap[slot];
-    if (sm.per == 1 && sm.G == (1 << 30)) {
-      // affine stream (sinks; gists when g == 1): position = base + u * stride1
-      const int p0 = sm.base + u0 * sm.stride1;
-      const unsigned short* k0 = kb + (int64_t)p0 * kst + kpiece * 8;
-      const unsigned short* v0 = vb + (int64_t)p0 * vst + pc * 8;
-      const int64_t kstep = (int64_t)sm.stride1 * kst, vstep = (int64_t)sm.stride1 * vst;
+    const bool affine = sm.per == 1 && sm.G == (1 << 30);
 #pragma unroll
-      for (int it = 0; it < NKL; ++it)
-        kreg[it] = *reinterpret_cast<const u32x4*>(k0 + imin(krow0 + RPP * it, width - 1) * kstep);
-      if (vrole) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          vreg[a] = *reinterpret_cast<const u32x4*>(v0 + imin(4 * rg + a, width - 1) * vstep);
-      }
-      return;
-    }
-#pragma unroll
-    for (int it = 0; it < NKL; ++it) {
-      const int key = imin(krow0 + RPP * it, width - 1);
-      kreg[it] = *reinterpret_cast<const u32x4*>(kb + (int64_t)map_pos(sm, u0 + key) * kst + kpiece * 8);
-    }
-    if (vrole) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int key = imin(4 * rg + a, width - 1);
-        vreg[a] = *reinterpret_cast<const u32x4*>(vb + (int64_t)map_pos(sm, u0 + key) * vst + pc * 8);
-      }
+    for (int it = 0; it < C::NIW; ++it) {
+      const int wi = wave * C::NIW + it;
+      const int row = wi * C::RPI + srow;
+      const int key = imin(row, width - 1);
+      const int p = affine ? sm.base + (u0 + key) * sm.stride1 : map_pos(sm, u0 + key);
+      const unsigned short* kp = kb + (int64_t)p * kst + 8 * (sslot ^ swz_k<D>(row));
+      const unsigned short* vp = vb + (int64_t)p * vst + 8 * (sslot ^ swz_v(row));
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)kp, (lds_void_ptr)(Klds + buf * kBN * D + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)vp, (lds_void_ptr)(Vlds + buf * kBN * D + wi * 512), 16, 0, 0);
     }
   };
 
+  // Transposed-read roles for the V^T operand: this lane supplies the address
+  // of key row 4(g/2) + j/4 (+16 st, +8 for the second read), d-chunk
+  // 16(g%2) + 4(j%4) (+32 mt), where g = lane / 16, j = lane % 16.
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tr_row = 4 * (tg >> 1) + (tj >> 2);
+  const int tr_piece = 2 * (tg & 1) + ((tj & 3) >> 1);
+  const int tr_half = tj & 1;
+
   int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0;
-  if (cnt > 0) fetch(0, nslot, nkind, nu0, nwidth, ncode);
+  if (cnt > 0) fetch(0, 0, nslot, nkind, nu0, nwidth, ncode);
 
   for (int idx = 0; idx < cnt; ++idx) {
     const int slot = nslot, kind = nkind, u0 = nu0, width = nwidth, code = ncode;
-    unsigned short* Kb = Klds + (idx & 1) * (kBN * C::KP);
-    unsigned short* VTb = VTlds + (idx & 1) * (D * C::VTP);
-
-    // ---- registers -> LDS (K row-major, V transposed: 4 keys per 8-byte write)
-#pragma unroll
-    for (int it = 0; it < NKL; ++it)
-      *reinterpret_cast<u32x4*>(&Kb[(krow0 + RPP * it) * C::KP + kpiece * 8]) = kreg[it];
-    if (vrole) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dw = e >> 1;
-        unsigned lo, hi;
-        if (e & 1) {
-          lo = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
-          hi = (vreg[2][dw] >> 16) | (vreg[3][dw] & 0xffff0000u);
-        } else {
-          lo = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
-          hi = (vreg[2][dw] & 0xffffu) | (vreg[3][dw] << 16);
-        }
-        *reinterpret_cast<u32x2*>(&VTb[(pc * 8 + e) * C::VTP + 4 * rg]) = u32x2{lo, hi};
-      }
-    }
-    // One barrier per tile: it publishes this tile's buffer, and every wave
-    // has finished the tile before last, whose buffer the next write reuses.
+    const unsigned short* Kb = Klds + (idx & 1) * (kBN * D);
+    const unsigned short* Vb = Vlds + (idx & 1) * (kBN * D);
+    // One barrier per tile: this wave's loads of tile idx have landed (the
+    // barrier waits for them), and every wave is done with tile idx-1, whose
+    // buffer the next fetch overwrites.
     __syncthreads();
-    if (idx + 1 < cnt) fetch(idx + 1, nslot, nkind, nu0, nwidth, ncode);
+    if (idx + 1 < cnt) fetch(idx + 1, (idx + 1) & 1, nslot, nkind, nu0, nwidth, ncode);
 
     // ---- S^T = K Q^T : two 32x32 tiles (keys 0..31, 32..63) x this wave's 32 queries
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Kb[n * C::KP + 8 * h2 + 16 * ks]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Kb[(32 + n) * C::KP + 8 * h2 + 16 * ks]);
+      const int pc = h2 + 2 * ks;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Kb[n * D + 8 * (pc ^ swz_k<D>(n))]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Kb[(32 + n) * D + 8 * (pc ^ swz_k<D>(32 + n))]);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
     }
@@ -268,12 +247,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     // ---- O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
-      const unsigned short* vrow = &VTb[(32 * mt + n) * C::VTP];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * st + 4 * h2);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * st + 8 + 4 * h2);
-        const u32x4 w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const int r0 = 16 * st + tr_row, r1 = r0 + 8;
+        const int pc = 4 * mt + tr_piece;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr)(Vb + r0 * D + 8 * (pc ^ swz_v(r0)) + 4 * tr_half));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_ptr)(Vb + r1 * D + 8 * (pc ^ swz_v(r1)) + 4 * tr_half));
+        const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+        const u32x4 w = u32x4{wl[0], wl[1], wh[0], wh[1]};
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[st],
                                                            oacc[mt], 0, 0, 0);
       }
