@@ -101,6 +101,12 @@ gsa_status make_lay(const gsa_layout* p, int L, int bn, Lay* out) {
     t0 += (l.len[s] + bn - 1) / bn;
   }
   l.nkt = t0;
+  for (int s = l.nstr; s < 4; ++s) {
+    l.tile0[s] = t0;
+    l.len[s] = 0;
+    l.kind[s] = K_RAW;
+    l.smap[s] = l.smap[l.nstr - 1];
+  }
   *out = l;
   return GSA_OK;
 }

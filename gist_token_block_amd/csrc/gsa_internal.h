@@ -126,12 +126,18 @@ __host__ __device__ inline int gist_group(const Lay& l, int u) { return fdiv(l.d
 
 // Key tile -> (stream slot, stream kind, first and one-past-last stream index).
 __host__ __device__ inline int tile_span(const Lay& l, int kt, int& kind, int& u0, int& u1) {
-  int s = 0;
-  while (s + 1 < l.nstr && kt >= l.tile0[s + 1]) ++s;
-  kind = l.kind[s];
-  u0 = (kt - l.tile0[s]) * l.bn;
-  u1 = imin(u0 + l.bn, l.len[s]);
+  // straight-line: unused slots have tile0 = nkt, so they never match
+  const int s = (kt >= l.tile0[1]) + (kt >= l.tile0[2]) + (l.nstr > 3 && kt >= l.tile0[3]);
+  const int t0 = s == 0 ? l.tile0[0] : s == 1 ? l.tile0[1] : s == 2 ? l.tile0[2] : l.tile0[3];
+  const int ln = s == 0 ? l.len[0] : s == 1 ? l.len[1] : s == 2 ? l.len[2] : l.len[3];
+  kind = s == 0 ? l.kind[0] : s == 1 ? l.kind[1] : s == 2 ? l.kind[2] : l.kind[3];
+  u0 = (kt - t0) * l.bn;
+  u1 = imin(u0 + l.bn, ln);
   return s;
+}
+
+__host__ __device__ inline StreamMap slot_map(const Lay& l, int s) {
+  return s == 0 ? l.smap[0] : s == 1 ? l.smap[1] : s == 2 ? l.smap[2] : l.smap[3];
 }
 
 // Is key (kind, stream index u, position p) visible to the query at i?

@@ -53,8 +53,12 @@ template <int D> struct Cfg {
   static constexpr int MT = D / 32;      // 32-row output tiles of O^T
 };
 // 16-byte piece p of key row r sits at slot p ^ swz(r).
+// K: rows of one 8-lane read phase hit 8 different 16-byte slots.  V: the
+// 4 rows x 2 pieces of a 16-lane transposed read, and the two 16-lane groups of
+// a 32-lane phase, hit disjoint slots.  Both swizzles depend on row % 16
+// (K) or row % 4 (V) only, so a lane's read offsets repeat for every tile.
 template <int D> __device__ inline int swz_k(int r) { return r & (D / 8 - 1); }
-__device__ inline int swz_v(int r) { return 2 * (r & 3); }
+template <int D> __device__ inline int swz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* glb_void_ptr;
@@ -139,22 +143,52 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   // re-read its last row: those keys are masked to -inf, so their P is 0 and
   // the duplicate (finite) values never count.
   const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  int koff[C::NIW], voff[C::NIW];   // element offset of the piece this lane fetches
+#pragma unroll
+  for (int it = 0; it < C::NIW; ++it) {
+    const int row = (wave * C::NIW + it) * C::RPI + srow;
+    koff[it] = 8 * (sslot ^ swz_k<D>(row));
+    voff[it] = 8 * (sslot ^ swz_v<D>(row));
+  }
   auto fetch = [&](int idx, int buf, int& slot, int& kind, int& u0, int& width, int& code) {
     const int kt = list[idx];
     code = codes[kt];
     int u1;
     slot = tile_span(l, kt, kind, u0, u1);
     width = u1 - u0;
-    const StreamMap sm = l.smap[slot];
+    const StreamMap sm = slot_map(l, slot);
     const bool affine = sm.per == 1 && sm.G == (1 << 30);
+    if (affine && width == kBN) {
+      // Full tile of an affine stream: row r sits at p0 + r * stride1.  Each
+      // load is a wave-uniform base (row block it) plus a 32-bit lane offset.
+      const int p0 = sm.base + u0 * sm.stride1;
+      const unsigned kstep = (unsigned)(sm.stride1 * kst) * 2u, vstep = (unsigned)(sm.stride1 * vst) * 2u;
+      const int row0 = wave * C::NIW * C::RPI + srow;
+#pragma unroll
+      for (int it = 0; it < C::NIW; ++it) {
+        const int wi = wave * C::NIW + it;
+        const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)p0 * kst) +
+                            (size_t)(wave * C::NIW + it) * C::RPI * kstep;
+        const char* vbase = reinterpret_cast<const char*>(vb + (int64_t)p0 * vst) +
+                            (size_t)(wave * C::NIW + it) * C::RPI * vstep;
+        const unsigned klane = (unsigned)srow * kstep + 2u * (unsigned)koff[it];
+        const unsigned vlane = (unsigned)srow * vstep + 2u * (unsigned)voff[it];
+        __builtin_amdgcn_global_load_lds((glb_void_ptr)(kbase + klane),
+                                         (lds_void_ptr)(Klds + buf * kBN * D + wi * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_ptr)(vbase + vlane),
+                                         (lds_void_ptr)(Vlds + buf * kBN * D + wi * 512), 16, 0, 0);
+      }
+      (void)row0;
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < C::NIW; ++it) {
       const int wi = wave * C::NIW + it;
       const int row = wi * C::RPI + srow;
       const int key = imin(row, width - 1);
       const int p = affine ? sm.base + (u0 + key) * sm.stride1 : map_pos(sm, u0 + key);
-      const unsigned short* kp = kb + (int64_t)p * kst + 8 * (sslot ^ swz_k<D>(row));
-      const unsigned short* vp = vb + (int64_t)p * vst + 8 * (sslot ^ swz_v(row));
+      const unsigned short* kp = kb + (int64_t)p * kst + koff[it];
+      const unsigned short* vp = vb + (int64_t)p * vst + voff[it];
       __builtin_amdgcn_global_load_lds((glb_void_ptr)kp, (lds_void_ptr)(Klds + buf * kBN * D + wi * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((glb_void_ptr)vp, (lds_void_ptr)(Vlds + buf * kBN * D + wi * 512), 16, 0, 0);
     }
@@ -167,6 +201,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   const int tr_row = 4 * (tg >> 1) + (tj >> 2);
   const int tr_piece = 2 * (tg & 1) + ((tj & 3) >> 1);
   const int tr_half = tj & 1;
+  int qk_off[C::KS], tr_off[C::MT];   // loop-invariant LDS element offsets
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qk_off[ks] = n * D + 8 * ((h2 + 2 * ks) ^ swz_k<D>(n));
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+    tr_off[mt] = tr_row * D + 8 * ((4 * mt + tr_piece) ^ swz_v<D>(tr_row)) + 4 * tr_half;
 
   int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0;
   if (cnt > 0) fetch(0, 0, nslot, nkind, nu0, nwidth, ncode);
@@ -181,16 +221,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     __syncthreads();
     if (idx + 1 < cnt) fetch(idx + 1, (idx + 1) & 1, nslot, nkind, nu0, nwidth, ncode);
 
-    // ---- S^T = K Q^T : two 32x32 tiles (keys 0..31, 32..63) x this wave's 32 queries
+    // ---- S^T = K Q^T: keys 0..31 into s0 first, then keys 32..63 into s1, so
+    // the softmax of the first half can start while the second half's MFMAs run.
     f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int pc = h2 + 2 * ks;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Kb[n * D + 8 * (pc ^ swz_k<D>(n))]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Kb[(32 + n) * D + 8 * (pc ^ swz_k<D>(32 + n))]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&Kb[qk_off[ks]]),
+                                                   qreg[ks], s0, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)   // rows n and 32 + n share their swizzle
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(&Kb[qk_off[ks] + 32 * D]), qreg[ks], s1, 0, 0, 0);
 
     // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
     if (code != 2 || width < kBN) {
@@ -200,65 +241,78 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
         const int key1 = key0 + 32;
         bool v0 = key0 < width, v1 = key1 < width;
         if (code != 2) {
-          if (v0) v0 = key_visible(l, i, kind, u0 + key0, map_pos(l.smap[slot], u0 + key0), selrow, selgrow);
-          if (v1) v1 = key_visible(l, i, kind, u0 + key1, map_pos(l.smap[slot], u0 + key1), selrow, selgrow);
+          if (v0) v0 = key_visible(l, i, kind, u0 + key0, map_pos(slot_map(l, slot), u0 + key0), selrow, selgrow);
+          if (v1) v1 = key_visible(l, i, kind, u0 + key1, map_pos(slot_map(l, slot), u0 + key1), selrow, selgrow);
         }
         if (!v0) s0[j] = -__builtin_inff();
         if (!v1) s1[j] = -__builtin_inff();
       }
     }
 
-    // ---- online softmax (base 2)
-    float mx = -__builtin_inff();
+    // ---- per half: online softmax (base 2), then O^T += V^T P^T for its 32 keys
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c2);
-    if (__ballot(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    for (int half = 0; half < 2; ++half) {
+      f32x16& sh = half ? s1 : s0;
+      float mx = sh[0];
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
-    }
-    m_run = m_new;
-    float psum = 0.f;
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sh[j]);
+      {  // max with the other half-wave (same queries, the other 16 keys)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // Lazy rescale: the reference max m_run only moves when some row's max
+      // exceeds it by more than 8 (log2 units), so P stays <= 256, which bf16
+      // and the fp32 sums hold without loss; most steps skip the rescale.
+      const float m_tile = mx * c2;
+      if (__ballot(m_tile > m_run + 8.f)) {
+        const float m_up = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_up);
+        l_run *= alpha;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s0[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], c2, -m_new));
-      s1[j] = __builtin_amdgcn_exp2f(fmaf(s1[j], c2, -m_new));
-      psum += s0[j] + s1[j];
-    }
-    l_run += psum;
+        for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
+        m_run = m_up;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sh[j] = __builtin_amdgcn_exp2f(fmaf(sh[j], c2, -m_run));
 
-    // P^T operands: step st uses tile st/2, accumulator regs 8(st%2)..+7
-    bf16x8 pk[4];
+      // P^T operands of steps 2 half + {0,1}: accumulator regs 8 x .. 8 x + 7.
+      // The row sum adds the bf16-rounded P actually fed to the PV product, so
+      // numerator and normaliser use the same weights.  (Packed words stay in
+      // scalars: bit-casting elements of a u32x4 here made the compiler feed
+      // the first element to every dot2.)
+      bf16x8 pk[2];
+      float psum = 0.f;
+      const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const f32x16& src = (st < 2) ? s0 : s1;
-      const int base = 8 * (st & 1);
-      u32x4 w;
-      w[0] = pack_bf16x2(src[base + 0], src[base + 1]);
-      w[1] = pack_bf16x2(src[base + 2], src[base + 3]);
-      w[2] = pack_bf16x2(src[base + 4], src[base + 5]);
-      w[3] = pack_bf16x2(src[base + 6], src[base + 7]);
-      pk[st] = __builtin_bit_cast(bf16x8, w);
-    }
+      for (int x = 0; x < 2; ++x) {
+        const int base = 8 * x;
+        const unsigned w0 = pack_bf16x2(sh[base + 0], sh[base + 1]);
+        const unsigned w1 = pack_bf16x2(sh[base + 2], sh[base + 3]);
+        const unsigned w2 = pack_bf16x2(sh[base + 4], sh[base + 5]);
+        const unsigned w3 = pack_bf16x2(sh[base + 6], sh[base + 7]);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, psum, false);
+        pk[x] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+      }
+      l_run += psum;
 
-    // ---- O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
+      // O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
+      for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int r0 = 16 * st + tr_row, r1 = r0 + 8;
-        const int pc = 4 * mt + tr_piece;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(Vb + r0 * D + 8 * (pc ^ swz_v(r0)) + 4 * tr_half));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_ptr)(Vb + r1 * D + 8 * (pc ^ swz_v(r1)) + 4 * tr_half));
-        const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
-        const u32x4 w = u32x4{wl[0], wl[1], wh[0], wh[1]};
-        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[st],
-                                                           oacc[mt], 0, 0, 0);
+        for (int x = 0; x < 2; ++x) {
+          const int st = 2 * half + x;   // rows 16 st + tr_row (+8) share the swizzle of tr_row
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st) * D));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st + 8) * D));
+          const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+          const u32x4 w = u32x4{wl[0], wl[1], wh[0], wh[1]};
+          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[x],
+                                                             oacc[mt], 0, 0, 0);
+        }
       }
     }
   }
