@@ -188,7 +188,7 @@ def run_decode(w, args, torch, gsa, copies=4):
     selg = (torch.empty((w.batch, w.hkv, 1, w.l2_top_k), dtype=torch.int32, device=dev)
             if w.hierarchical else None)
     o = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
-    wsb = torch.empty(gsa.decode_workspace_bytes(w.layout, w.batch, w.hq, w.hkv, w.d, L),
+    wsb = torch.zeros(gsa.decode_workspace_bytes(w.layout, w.batch, w.hq, w.hkv, w.d, L),
                       dtype=torch.uint8, device=dev)
 
     def step(s):

@@ -247,8 +247,8 @@ def attn_decode(layout: dict, q, k_cache, v_cache, sel=None, sel_groups=None,
     Hkv, kv_len = k_cache.shape[1], k_cache.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     need = decode_workspace_bytes(layout, B, Hq, Hkv, d, kv_len)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None:   # zero-filled once: the kernel leaves its counters at zero
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
         o = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None

@@ -8,33 +8,50 @@
 // segments -- sinks before the window, gists before the window, the kept
 // groups' level-1 gists before the window, the window itself, each unfolded
 // chunk's raws before the window -- so every row is read exactly once.  The
-// rows are cut into splits of 128; one workgroup (4 waves) per (split, KV
-// head, batch) stages 64 rows of K and V at a time to LDS with 16-byte loads
-// (a chunk's raws are contiguous in the [B, Hkv, kv_len, d] cache), and each
-// wave takes 16 of them for all G query heads of the KV group at once:
+// rows are cut into a few long splits (about two workgroups per CU in all);
+// one workgroup (4 waves) per (split, KV head, batch) streams its rows in
+// 64-row blocks of K and V straight into LDS, double buffered
+// (global_load_lds_dwordx4: the next block flies while this one is computed;
+// one chunk's raws are
+// contiguous in the [B, Hkv, kv_len, d] cache), and each wave takes 16 rows
+// of a block for all G query heads of the KV group at once:
 //   S^T (16 keys x 16 head slots) = K q^T   v_mfma_f32_16x16x32_bf16
 //   O^T (16 d x 16 head slots)   += V^T P^T v_mfma_f32_16x16x16_bf16
 // The S accumulator layout (lane = head slot, 4 keys) is exactly the B operand
-// layout of the 16x16x16 product, so P never leaves registers.  Waves keep
-// separate (max, sum, O) partials; they are merged in LDS, written to the
-// workspace, and a second kernel merges the splits (log-sum-exp weights).
+// layout of the 16x16x16 product, so P never leaves registers; the V^T operand
+// comes from the row-major V block through ds_read_b64_tr_b16.  Waves keep
+// separate (max, sum, O) partials, merged in LDS into the split's partial; the
+// last split of a (batch, KV head) to finish (a counter in the workspace)
+// merges all splits with log-sum-exp weights and writes the output.
 #include "gsa_internal.h"
 
 namespace gsa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;          // rows staged per step
-constexpr int kRowsPerSplit = 128;
+constexpr int kRows = 64;          // rows per staged block (double buffered)
 constexpr int kMaxSeg = 3 + 64 + 64;
+constexpr int kMaxSplit = 64;      // splits per (batch, KV head) the merge step holds
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* glb_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 template <int D> struct DCfg {
-  static constexpr int KP = D + 8;
-  static constexpr int VP = D + 8;
-  static constexpr int PPR = D / 8;
-  static constexpr int KS = D / 32;   // k-steps of the QK product (K = 32)
-  static constexpr int MT = D / 16;   // 16-row tiles of O^T
+  static constexpr int PPR = D / 8;          // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;       // rows per 1 KB wave load
+  static constexpr int NIW = kRows / RPI / 4;  // wave loads per block per wave
+  static constexpr int KS = D / 32;          // k-steps of the QK product (K = 32)
+  static constexpr int MT = D / 16;          // 16-row tiles of O^T
 };
+// Row r keeps its 16-byte piece p at slot p ^ swz(r) (see the prefill kernel).
+template <int D> __device__ inline int dswz_k(int r) { return r & (D / 8 - 1); }
+template <int D> __device__ inline int dswz_v(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+
+__device__ inline void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Visible-row segments of one (batch, KV head).
 struct Segs {
@@ -45,19 +62,26 @@ struct Segs {
 };
 
 __device__ inline int seg_pos(const Lay& l, const Segs& s, int v) {
-  int j = 0;
-  while (j + 1 < s.n && s.start[j + 1] <= v) ++j;
-  const int off = v - s.start[j];
-  return s.kind[j] < 0 ? s.base[j] + off : pos_of(l, s.kind[j], s.base[j] + off);
+  int lo = 0, hi = s.n - 1;            // last segment with start <= v
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s.start[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  const int off = v - s.start[lo];
+  return s.kind[lo] < 0 ? s.base[lo] + off : pos_of(l, s.kind[lo], s.base[lo] + off);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_decode_split(
+// Workspace: int counters [B*Hkv] (zero between calls), then partials
+// [B*Hkv][nsplit][G][D + 2] (O, then max in log2 units, then sum).
+template <int D, typename TO>
+__global__ __launch_bounds__(kThreads) void k_decode(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qsh,
     const unsigned short* __restrict__ kc, int64_t ksb, int64_t kst, int64_t ksh,
     const unsigned short* __restrict__ vc, int64_t vsb, int64_t vst, int64_t vsh, int Hq, int Hkv,
     int kv_len, const int* __restrict__ sel, const int* __restrict__ selg, float c2,
-    float* __restrict__ ws, int nsplit) {
+    int* __restrict__ counters, float* __restrict__ part, int nsplit, int rows_per_split,
+    TO* __restrict__ o, int64_t osb, int64_t osh, float* __restrict__ lse) {
   using C = DCfg<D>;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -65,11 +89,24 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
   const int G = Hq / Hkv;
   const int i = kv_len - 1;
   const int lo = imax(0, i - l.W1 + 1);
+  const size_t gidx = (size_t)b * Hkv + h;
 
   __shared__ Segs segs;
-  __shared__ __attribute__((aligned(16))) unsigned short stage[kRows * (C::KP + C::VP)];
-  unsigned short* Klds = stage;
-  unsigned short* Vlds = stage + kRows * C::KP;
+  __shared__ int rowpos[2][kRows];
+  __shared__ int ssel[64], sselg[64];
+  __shared__ int am_last;
+  __shared__ float wstat[128];
+  // Two staging buffers, K then V rows of one block each.  They are separate
+  // arrays indexed only statically: the compiler can then tell the prefetch's
+  // LDS writes from the reads of the current block and does not make every
+  // LDS read wait for the prefetch.
+  __shared__ __attribute__((aligned(1024))) unsigned short stage[2 * kRows * D];
+  __shared__ __attribute__((aligned(1024))) unsigned short stage1[2 * kRows * D];
+
+  // selections first, all at once (the table build below reads them serially)
+  if (tid < l.k) ssel[tid] = sel[gidx * l.k + tid];
+  if (selg && tid >= 64 && tid - 64 < l.k2) sselg[tid - 64] = selg[gidx * l.k2 + tid - 64];
+  __syncthreads();
 
   if (tid == 0) {
     int n = 0, tot = 0;
@@ -82,7 +119,6 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
       ++n;
     };
     add(-1, 0, imin(l.S, lo));
-    const size_t srow = (size_t)b * Hkv + h;
     if (l.G2 == 0) {
       add(K_GIST, 0, count_below(l, K_GIST, lo));
     } else {
@@ -90,21 +126,54 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
       const int gl = count_below(l, K_GIST, lo), per = l.G2 * l.g;
       const int ngr = count_below(l, K_GIST2, i) / l.g2;   // groups complete before i
       for (int e = 0; e < l.k2; ++e) {
-        const int gr = selg[srow * l.k2 + e];
+        const int gr = sselg[e];
         if (gr >= 0 && gr < ngr) add(K_GIST, gr * per, iclamp(gl - gr * per, 0, per));
       }
     }
     add(-1, lo, i - lo + 1);
     const int nch = count_below(l, K_GIST, i) / l.g;          // chunks complete before i
     for (int e = 0; e < l.k; ++e) {
-      const int m = sel[srow * l.k + e];
+      const int m = ssel[e];
       if (m < 0 || m >= nch) continue;   // ids outside the candidates are ignored
       const int st = pos_of(l, K_RAW, m * l.c);
       add(-1, st, iclamp(lo - st, 0, l.c));
     }
     segs.start[n] = tot;
     segs.n = n;
+    am_last = 0;
   }
+  __syncthreads();
+  const int total = segs.start[segs.n];
+  const int v_begin = imin(split * rows_per_split, total);
+  const int v_end = imin(v_begin + rows_per_split, total);
+  const int nblk = (v_end - v_begin + kRows - 1) / kRows;
+
+  const unsigned short* kb = kc + b * ksb + h * ksh;
+  const unsigned short* vb = vc + b * vsb + h * vsh;
+  const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  // Row positions of block `blk` (rows past the end repeat the last one; their
+  // logits are masked, so the duplicate never counts), then its K and V rows
+  // straight into LDS buffer blk % 2.
+  auto positions = [&](int blk) {
+    if (tid < kRows) rowpos[blk & 1][tid] = seg_pos(l, segs, imin(v_begin + blk * kRows + tid, v_end - 1));
+  };
+  auto fetch = [&](int blk, unsigned short* Kd) {
+    unsigned short* Vd = Kd + kRows * D;
+#pragma unroll
+    for (int it = 0; it < C::NIW; ++it) {
+      const int wi = wave * C::NIW + it;
+      const int row = wi * C::RPI + srow;
+      const int p = rowpos[blk & 1][row];
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)(kb + (int64_t)p * kst + 8 * (sslot ^ dswz_k<D>(row))),
+                                       (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)(vb + (int64_t)p * vst + 8 * (sslot ^ dswz_v<D>(row))),
+                                       (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
+    }
+  };
+  if (nblk > 0) positions(0);
+  if (nblk > 1) positions(1);
+  __syncthreads();
+  if (nblk > 0) fetch(0, stage);
 
   // q^T operands: lane = head slot `col` (valid if < G), d = 8 grp + 32 ks
   bf16x8 qreg[C::KS];
@@ -117,85 +186,98 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
       qreg[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __syncthreads();
-
-  const int total = segs.start[segs.n];
-  const int v_begin = split * kRowsPerSplit;
-  const int v_end = imin(v_begin + kRowsPerSplit, total);
-  const unsigned short* kb = kc + b * ksb + h * ksh;
-  const unsigned short* vb = vc + b * vsb + h * vsh;
-
+  // transposed-read roles for the V^T operand of the 16x16x16 product: this
+  // lane supplies row 4 grp + j/4 (+16 wave), d-chunk 4 (j%4) (+16 mt)
+  const int tj = lane & 15;
+  const int trow = 4 * grp + (tj >> 2);
+  // Per-lane element offsets of the K and V^T operands inside a block.  The
+  // empty asm makes each opaque, so every LDS read is one offset from its
+  // buffer: the compiler then keeps the buffer's alias scope on it (a long
+  // chain of derived addresses loses it, and an unscoped read waits for
+  // every copy in flight, the prefetch included).
+  int k_off[C::KS], tr_off[C::MT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int row = 16 * wave + col, pc = grp + 4 * ks;
+    k_off[ks] = row * D + 8 * (pc ^ dswz_k<D>(row));
+    asm volatile("" : "+v"(k_off[ks]));
+  }
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) {
+    const int row = 16 * wave + trow, pc = 2 * mt + ((tj & 3) >> 1);
+    tr_off[mt] = row * D + 8 * (pc ^ dswz_v<D>(row)) + 4 * (tj & 1);
+    asm volatile("" : "+v"(tr_off[mt]));
+  }
   f32x4 oacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig, l_run = 0.f;
 
-  for (int vb0 = v_begin; vb0 < v_end; vb0 += kRows) {
-    constexpr int RPP = kThreads / C::PPR;
-#pragma unroll
-    for (int it = 0; it < kRows / RPP; ++it) {
-      const int rr = tid / C::PPR + RPP * it;
-      const int piece = tid % C::PPR;
-      const int vv = vb0 + rr;
-      u32x4 wk = u32x4{0u, 0u, 0u, 0u}, wv = wk;
-      if (vv < v_end) {
-        const int p = seg_pos(l, segs, vv);
-        wk = *reinterpret_cast<const u32x4*>(kb + (int64_t)p * kst + piece * 8);
-        wv = *reinterpret_cast<const u32x4*>(vb + (int64_t)p * vst + piece * 8);
-      }
-      *reinterpret_cast<u32x4*>(&Klds[rr * C::KP + piece * 8]) = wk;
-      *reinterpret_cast<u32x4*>(&Vlds[rr * C::VP + piece * 8]) = wv;
-    }
+  auto step = [&](int blk, const unsigned short* Kb, unsigned short* next) {
+    // One barrier per block: this wave's copies of block blk have landed
+    // (the wait), so after the barrier all of them have, every wave is done
+    // with block blk - 1 (whose buffer the next fetch reuses), and the
+    // positions of blk + 1 are set.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
+    if (blk + 1 < nblk) fetch(blk + 1, next);
+    if (blk + 2 < nblk) positions(blk + 2);
+    const unsigned short* Vb = Kb + kRows * D;
     const int r0 = 16 * wave;
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Klds[(r0 + col) * C::KP + 8 * grp + 32 * ks]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + k_off[ks]);
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s, 0, 0, 0);
     }
-    // s[e]: key row r0 + 4 grp + e, head slot col
+    // s[e]: key row r0 + 4 grp + e of the block, head slot col
+    const int vrow0 = v_begin + blk * kRows + r0 + 4 * grp;
     float mx = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (vb0 + r0 + 4 * grp + e >= v_end) s[e] = -__builtin_inff();
+      if (vrow0 + e >= v_end) s[e] = -__builtin_inff();
       mx = fmaxf(mx, s[e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const float m_new = fmaxf(m_run, mx * c2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float ps = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -m_new));
-      ps += s[e];
-    }
+    for (int e = 0; e < 4; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -m_new));
+    const unsigned w0 = pack_bf16x2(s[0], s[1]), w1 = pack_bf16x2(s[2], s[3]);
+    const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+    float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.f, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, ps, false);
     ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+      ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    const u32x2 pw = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-    const bf16x4 pb = __builtin_bit_cast(bf16x4, pw);
+    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
       oacc[mt] *= alpha;
-      const int dcol = 16 * mt + col;
-      const unsigned short* vr = &Vlds[(r0 + 4 * grp) * C::VP + dcol];
-      const unsigned w0 = (unsigned)vr[0] | ((unsigned)vr[C::VP] << 16);
-      const unsigned w1 = (unsigned)vr[2 * C::VP] | ((unsigned)vr[3 * C::VP] << 16);
-      const bf16x4 a = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
-      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, oacc[mt], 0, 0, 0);
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(Vb + tr_off[mt]));
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, pb), oacc[mt], 0, 0, 0);
     }
-    __syncthreads();
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, stage, stage1);
+    if (blk + 1 < nblk) step(blk + 1, stage1, stage);
   }
+  __syncthreads();   // staging memory is reused below
 
-  // ---- merge the 4 waves' partials (reuse the K/V staging memory)
-  float* cm = reinterpret_cast<float*>(stage);         // [4][16]
-  float* cl = cm + 4 * 16;                             // [4][16]
-  float* co = cl + 4 * 16;                             // [4][16][D]
-  static_assert(kRows * (DCfg<D>::KP + DCfg<D>::VP) * 2 >= (128 + 64 * D) * 4, "LDS reuse too small");
+  // ---- merge the 4 waves' partials, write this split's partial
+  float* cm = wstat;                                   // [4][16]
+  float* cl = wstat + 4 * 16;                          // [4][16]
+  float* co = reinterpret_cast<float*>(stage);         // [4][16][D]
+  static_assert(2 * kRows * D * 2 >= 64 * D * 4, "LDS reuse too small");
+  static_assert(2 * kRows * D * 2 >= (2 * kMaxSplit * 16 + 32) * 4, "LDS reuse too small");
   if (grp == 0) {
     cm[wave * 16 + col] = m_run;
     cl[wave * 16 + col] = l_run;
@@ -205,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
 #pragma unroll
     for (int e = 0; e < 4; ++e) co[(wave * 16 + col) * D + 16 * mt + 4 * grp + e] = oacc[mt][e];
   __syncthreads();
+  float* mypart = part + (gidx * nsplit + split) * G * (D + 2);
   for (int x = tid; x < G * D; x += kThreads) {
     const int hd = x / D, dd = x - hd * D;
     float M = kNegBig;
@@ -215,39 +298,73 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(
       L += cl[w * 16 + hd] * f;
       O += co[(w * 16 + hd) * D + dd] * f;
     }
-    float* part = ws + ((((size_t)b * Hkv + h) * nsplit + split) * G + hd) * (D + 2);
-    part[dd] = O;
+    // device-scope stores: coherent across the XCDs' L2s without a cache-wide
+    // write-back (a device-scope fence here costs far more than the kernel)
+    st_dev(&mypart[hd * (D + 2) + dd], O);
     if (dd == 0) {
-      part[D] = M;
-      part[D + 1] = L;
+      st_dev(&mypart[hd * (D + 2) + D], M);
+      st_dev(&mypart[hd * (D + 2) + D + 1], L);
     }
   }
-}
 
-template <int D, typename TO>
-__global__ __launch_bounds__(D) void k_decode_combine(const float* __restrict__ ws, int Hq, int Hkv,
-                                                      int nsplit, TO* __restrict__ o, int64_t osb,
-                                                      int64_t osh, float* __restrict__ lse) {
-  const int hq = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
-  const int G = Hq / Hkv, h = hq / G, hd = hq - h * G;
-  const float* base = ws + (((size_t)b * Hkv + h) * nsplit * G + hd) * (D + 2);
-  const size_t step = (size_t)G * (D + 2);
-  float M = kNegBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * step + D]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float f = __builtin_amdgcn_exp2f(base[s * step + D] - M);
-    L += base[s * step + D + 1] * f;
-    O += base[s * step + dd] * f;
+  // ---- the last split of this (batch, KV head) merges all partials: every
+  // thread's partial stores have completed before the barrier that precedes
+  // the counter update, and the merging workgroup reads them after seeing
+  // the count, with device-scope loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&counters[gidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    am_last = prev == nsplit - 1;
   }
-  const float val = O / L;
-  TO* orow = o + b * osb + hq * osh;
-  if constexpr (sizeof(TO) == 4) {
-    orow[dd] = val;
-  } else {
-    orow[dd] = (TO)(pack_bf16x2(val, 0.f) & 0xffffu);
+  __syncthreads();
+  if (!am_last) return;
+  const float* gp = part + gidx * nsplit * G * (D + 2);
+  // (max, sum) of every split and head in one parallel load, then the weights
+  float* sm = reinterpret_cast<float*>(stage);       // [nsplit][G] maxima, then weights
+  float* sl = sm + kMaxSplit * 16;                   // [nsplit][G] sums
+  float* hm = sl + kMaxSplit * 16;                   // [G] merged max, [G] merged sum
+  for (int x = tid; x < nsplit * G; x += kThreads) {
+    const float* pp = gp + x * (D + 2);
+    sm[x] = ld_dev(&pp[D]);
+    sl[x] = ld_dev(&pp[D + 1]);
   }
-  if (lse && dd == 0) lse[(size_t)b * Hq + hq] = (M + __log2f(L)) * kLn2;
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegBig;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, sm[sp * G + tid]);
+    float L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) L += sl[sp * G + tid] * __builtin_amdgcn_exp2f(sm[sp * G + tid] - M);
+    hm[tid] = M;
+    hm[16 + tid] = L;
+  }
+  __syncthreads();
+  for (int x = tid; x < nsplit * G; x += kThreads) sm[x] = __builtin_amdgcn_exp2f(sm[x] - hm[x % G]);
+  __syncthreads();
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int hd = x / D, dd = x - hd * D;
+    float O = 0.f;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+      float po[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {   // all loads of the batch in flight together
+        const int sp = imin(sp0 + j, nsplit - 1);
+        po[j] = ld_dev(&gp[(sp * G + hd) * (D + 2) + dd]);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sp0 + j < nsplit) O += po[j] * sm[(sp0 + j) * G + hd];
+    }
+    const float val = O / hm[16 + hd];
+    TO* orow = o + b * osb + (int64_t)(h * G + hd) * osh;
+    if constexpr (sizeof(TO) == 4) {
+      orow[dd] = val;
+    } else {
+      orow[dd] = (TO)(pack_bf16x2(val, 0.f) & 0xffffu);
+    }
+    if (lse && dd == 0) lse[(size_t)b * Hq + h * G + hd] = (hm[hd] + __log2f(hm[16 + hd])) * kLn2;
+  }
+  if (tid == 0) __hip_atomic_store(&counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Upper bound of the visible rows of one decode query.
@@ -260,6 +377,25 @@ int row_bound(const Lay& l, int kv_len) {
   return (int)n;
 }
 
+size_t counters_bytes(int B, int Hkv) { return ((size_t)B * Hkv * sizeof(int) + 255) / 256 * 256; }
+
+// Splits per (batch, KV head): enough workgroups for about two per CU in total,
+// each streaming a long run of 64-row blocks.
+int plan_splits(int B, int Hkv, int rows, int* rows_per_split) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  const int groups = imax(1, B * Hkv);
+  int ns = iclamp((2 * cus + groups - 1) / groups, 1, kMaxSplit);
+  ns = imin(ns, imax(1, (rows + kRows - 1) / kRows));
+  const int per = (rows + ns - 1) / ns;
+  *rows_per_split = (per + kRows - 1) / kRows * kRows;
+  return (rows + *rows_per_split - 1) / *rows_per_split;
+}
+
 }  // namespace
 }  // namespace gsa
 
@@ -269,8 +405,9 @@ extern "C" size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B
                                              int32_t d, int32_t kv_len) {
   Lay l;
   if (make_lay(layout, kv_len, 64, &l) != GSA_OK || kv_len < 1 || Hkv < 1 || Hq % Hkv) return 0;
-  const int ns = (row_bound(l, kv_len) + kRowsPerSplit - 1) / kRowsPerSplit;
-  return (size_t)B * Hkv * ns * (Hq / Hkv) * (d + 2) * sizeof(float);
+  int rps;
+  const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
+  return counters_bytes(B, Hkv) + (size_t)B * Hkv * ns * (Hq / Hkv) * (d + 2) * sizeof(float);
 }
 
 extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
@@ -299,31 +436,27 @@ extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gs
   if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
   const size_t need = gsa_decode_workspace_bytes(layout, B, Hq, Hkv, d, kv_len);
   if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  const int ns = (row_bound(l, kv_len) + kRowsPerSplit - 1) / kRowsPerSplit;
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
+  int rps;
+  const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
   hipStream_t s = (hipStream_t)stream;
   const float c2 = scale * kLog2e;
-  float* w = (float*)ws;
-#define GSA_SPLIT(D)                                                                                 \
-  hipLaunchKernelGGL((k_decode_split<D>), dim3(ns, Hkv, B), dim3(kThreads), 0, s, l,                  \
+  int* counters = (int*)ws;
+  float* part = (float*)((char*)ws + counters_bytes(B, Hkv));
+#define GSA_DECODE(D, TO)                                                                             \
+  hipLaunchKernelGGL((k_decode<D, TO>), dim3(ns, Hkv, B), dim3(kThreads), 0, s, l,                    \
                      (const unsigned short*)q.ptr, q.stride_b, q.stride_h,                            \
                      (const unsigned short*)k_cache.ptr, k_cache.stride_b, k_cache.stride_t,          \
                      k_cache.stride_h, (const unsigned short*)v_cache.ptr, v_cache.stride_b,          \
-                     v_cache.stride_t, v_cache.stride_h, Hq, Hkv, kv_len, sel, sel_groups, c2, w, ns)
-#define GSA_COMBINE(D, TO)                                                                           \
-  hipLaunchKernelGGL((k_decode_combine<D, TO>), dim3(Hq, B), dim3(D), 0, s, w, Hq, Hkv, ns,           \
-                     (TO*)o.ptr, o.stride_b, o.stride_h, lse)
+                     v_cache.stride_t, v_cache.stride_h, Hq, Hkv, kv_len, sel, sel_groups, c2,        \
+                     counters, part, ns, rps, (TO*)o.ptr, o.stride_b, o.stride_h, lse)
   if (d == 128) {
-    GSA_SPLIT(128);
-    if ((st = launch_status("gsa_attn_decode (split)")) != GSA_OK) return st;
-    if (o.dtype == GSA_F32) GSA_COMBINE(128, float);
-    else GSA_COMBINE(128, unsigned short);
+    if (o.dtype == GSA_F32) GSA_DECODE(128, float);
+    else GSA_DECODE(128, unsigned short);
   } else {
-    GSA_SPLIT(64);
-    if ((st = launch_status("gsa_attn_decode (split)")) != GSA_OK) return st;
-    if (o.dtype == GSA_F32) GSA_COMBINE(64, float);
-    else GSA_COMBINE(64, unsigned short);
+    if (o.dtype == GSA_F32) GSA_DECODE(64, float);
+    else GSA_DECODE(64, unsigned short);
   }
-#undef GSA_SPLIT
-#undef GSA_COMBINE
-  return launch_status("gsa_attn_decode (combine)");
+#undef GSA_DECODE
+  return launch_status("gsa_attn_decode");
 }

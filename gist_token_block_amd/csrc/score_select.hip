@@ -9,12 +9,13 @@
 // gists, of q.k * scale; the query-head mean is taken first (qbar), which is
 // the same number by linearity.  Order: score descending, then id ascending.
 //
-// One workgroup (4 waves) per (batch, KV head, query row).  Candidates are
-// scored 64 at a time; lanes of a row group read one key row with 16-byte
-// loads.  Each wave keeps a running best-64 list across lanes, merging every
-// scored batch with a 64-lane bitonic network (sort the batch, take the
-// element-wise better of the running list and the reversed batch, then a
-// bitonic merge).  The four waves' lists meet in LDS and wave 0 merges them.
+// One workgroup per (batch, KV head, query row), with one wave per 64
+// candidates up to 16 waves, so every gist key of the row is in flight at
+// once.  Lanes of a row group read one key row with 16-byte loads.  Each wave
+// keeps a running best-64 list across lanes, merging every scored batch with a
+// 64-lane bitonic network (sort the batch, take the element-wise better of
+// the running list and the reversed batch, then a bitonic merge).  The waves'
+// lists then meet in LDS in a log-depth merge tree.
 #include <float.h>
 #include <limits.h>
 
@@ -23,8 +24,7 @@
 namespace gsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kMaxWaves = 16;
 
 __device__ inline bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
@@ -86,21 +86,26 @@ __device__ inline void wave_sort_int_asc(int& v) {
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int n = 4;
+  __device__ static void unpack(const u32x4 w, float* out) {
+    out[0] = __uint_as_float(w[0]); out[1] = __uint_as_float(w[1]);
+    out[2] = __uint_as_float(w[2]); out[3] = __uint_as_float(w[3]);
+  }
   __device__ static void load(const float* p, float* out) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
-    out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[3];
+    unpack(*reinterpret_cast<const u32x4*>(p), out);
   }
   __device__ static float one(const float* p) { return *p; }
 };
 template <> struct Vec16<unsigned short> {
   static constexpr int n = 8;
-  __device__ static void load(const unsigned short* p, float* out) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+  __device__ static void unpack(const u32x4 w, float* out) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       out[2 * j] = lo_bf16(w[j]);
       out[2 * j + 1] = hi_bf16(w[j]);
     }
+  }
+  __device__ static void load(const unsigned short* p, float* out) {
+    unpack(*reinterpret_cast<const u32x4*>(p), out);
   }
   __device__ static float one(const unsigned short* p) { return bf16_to_f32(*p); }
 };
@@ -127,7 +132,7 @@ struct InGroupCands {      // two levels, level 1: chunks of the kept groups
   __device__ int id(int e) const { return chunk(e); }
 };
 
-// Score `ncand` candidates and leave the wave-merged best-64 list in lanes of
+// Score `ncand` candidates and leave the merged best-64 list in the lanes of
 // wave 0 (rs, ri); every wave returns after the block-wide merge.
 template <typename T, int D, typename Cands>
 __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const float* __restrict__ qbar,
@@ -138,32 +143,51 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
   constexpr int LPR = D / EPL;       // lanes per key row
   constexpr int RPI = 64 / LPR;      // key rows per wave instruction
   constexpr int ITER = LPR;          // instructions per batch of 64 rows
-  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  const int lane = __lane_id(), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int sub = lane % LPR, grp = lane / LPR;
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qbar[sub * EPL + e];
 
-  rs = -FLT_MAX;
-  ri = INT_MAX;
   rs = -__builtin_inff();
+  ri = INT_MAX;
   const int nbatch = (ncand + 63) / 64;
   const int ng = cands.ngist();
-  for (int bi = wave; bi < nbatch; bi += kWaves) {
+  for (int bi = wave; bi < nbatch; bi += nw) {
     float part[ITER];
+    if (ITER <= 16 && ng == 1) {
+      // one gist per candidate: issue every row load of the batch, then reduce
+      constexpr int NB = ITER <= 16 ? ITER : 1;   // (f32 with d = 128 takes the loop below)
+      u32x4 raw[NB];
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int e = bi * 64 + grp + RPI * it;
-      float acc = 0.f;
-      if (e < ncand) {
-        for (int t = 0; t < ng; ++t) {
-          float kv[EPL];
-          V::load(kb + (int64_t)cands.pos(e, t) * kst + sub * EPL, kv);
-#pragma unroll
-          for (int x = 0; x < EPL; ++x) acc = fmaf(qv[x], kv[x], acc);
-        }
+      for (int it = 0; it < NB; ++it) {
+        const int e = imin(bi * 64 + grp + RPI * it, ncand - 1);
+        raw[it] = *reinterpret_cast<const u32x4*>(kb + (int64_t)cands.pos(e, 0) * kst + sub * EPL);
       }
-      part[it] = acc;
+#pragma unroll
+      for (int it = 0; it < NB; ++it) {
+        float kv[EPL];
+        V::unpack(raw[it], kv);
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc = fmaf(qv[x], kv[x], acc);
+        part[it] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int e = bi * 64 + grp + RPI * it;
+        float acc = 0.f;
+        if (e < ncand) {
+          for (int t = 0; t < ng; ++t) {
+            float kv[EPL];
+            V::load(kb + (int64_t)cands.pos(e, t) * kst + sub * EPL, kv);
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) acc = fmaf(qv[x], kv[x], acc);
+          }
+        }
+        part[it] = acc;
+      }
     }
     float mine = 0.f;
 #pragma unroll
@@ -184,17 +208,22 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
     wave_sort_best_first(s, id);
     wave_merge(rs, ri, s, id);
   }
+  // merge tree: at step st, wave w (w % 2st == 0) absorbs wave w + st
   lds_s[wave * 64 + lane] = rs;
   lds_i[wave * 64 + lane] = ri;
   __syncthreads();
-  if (wave == 0) {
-    for (int w = 1; w < kWaves; ++w) wave_merge(rs, ri, lds_s[w * 64 + lane], lds_i[w * 64 + lane]);
+  for (int st = 1; st < nw; st <<= 1) {
+    if ((wave & (2 * st - 1)) == 0 && wave + st < nw) {
+      wave_merge(rs, ri, lds_s[(wave + st) * 64 + lane], lds_i[(wave + st) * 64 + lane]);
+      lds_s[wave * 64 + lane] = rs;
+      lds_i[wave * 64 + lane] = ri;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void k_score_select(
+__global__ __launch_bounds__(64 * kMaxWaves) void k_score_select(
     Lay l, const T* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh, const T* __restrict__ k,
     int64_t ksb, int64_t kst, int64_t ksh, int Hq, int Hkv, int q_begin, int q_len, float scale,
     int* __restrict__ sel, int* __restrict__ selg, float* __restrict__ scores, int ncols) {
@@ -202,12 +231,13 @@ __global__ __launch_bounds__(kThreads) void k_score_select(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / Hkv;
   const int i = q_begin + r;
+  const int nthr = blockDim.x;
   __shared__ float qbar[D];
-  __shared__ float lds_s[kWaves * 64];
-  __shared__ int lds_i[kWaves * 64];
+  __shared__ float lds_s[kMaxWaves * 64];
+  __shared__ int lds_i[kMaxWaves * 64];
   __shared__ int kept[64];
 
-  for (int e = tid; e < D; e += kThreads) {
+  for (int e = tid; e < D; e += nthr) {
     float s = 0.f;
     for (int g = 0; g < G; ++g) s += Vec16<T>::one(q + b * qsb + r * qst + (int64_t)(h * G + g) * qsh + e);
     qbar[e] = s / (float)G;
@@ -222,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_score_select(
     const int ncand = i >= l.S ? (i - l.S) / l.P : 0;
     float* so = scores ? scores + row * ncols : nullptr;
     if (so)
-      for (int e = ncand + tid; e < ncols; e += kThreads) so[e] = -__builtin_inff();
+      for (int e = ncand + tid; e < ncols; e += nthr) so[e] = -__builtin_inff();
     ChunkCands cands{&l};
     score_and_rank<T, D>(kb, kst, qbar, ncand, scale / (float)l.g, cands, so, lds_s, lds_i, rs, ri);
     if (wave == 0) {
@@ -237,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void k_score_select(
   const int ng2 = i >= l.S ? (i - l.S) / l.P2 : 0;
   float* so = scores ? scores + row * ncols : nullptr;
   if (so)
-    for (int e = ng2 + tid; e < ncols; e += kThreads) so[e] = -__builtin_inff();
+    for (int e = ng2 + tid; e < ncols; e += nthr) so[e] = -__builtin_inff();
   GroupCands gc{&l};
   score_and_rank<T, D>(kb, kst, qbar, ng2, scale / (float)l.g2, gc, so, lds_s, lds_i, rs, ri);
   __shared__ int nkept;
@@ -263,7 +293,12 @@ __global__ __launch_bounds__(kThreads) void k_score_select(
 template <typename T, int D>
 void launch(const Lay& l, const gsa_tensor& q, const gsa_tensor& k, int B, int Hq, int Hkv, int q_begin,
             int q_len, float scale, int* sel, int* selg, float* scores, int ncols, hipStream_t st) {
-  hipLaunchKernelGGL((k_score_select<T, D>), dim3(q_len, Hkv, B), dim3(kThreads), 0, st, l,
+  // one wave per 64 candidates of the busiest row (either level), 1..16 waves
+  const int i_max = q_begin + q_len - 1;
+  int nmax = l.G2 == 0 ? (i_max >= l.S ? (i_max - l.S) / l.P : 0)
+                       : imax(i_max >= l.S ? (i_max - l.S) / l.P2 : 0, l.k2 * l.G2);
+  const int waves = iclamp((nmax + 63) / 64, 1, kMaxWaves);
+  hipLaunchKernelGGL((k_score_select<T, D>), dim3(q_len, Hkv, B), dim3(64 * waves), 0, st, l,
                      (const T*)q.ptr, q.stride_b, q.stride_t, q.stride_h, (const T*)k.ptr, k.stride_b,
                      k.stride_t, k.stride_h, Hq, Hkv, q_begin, q_len, scale, sel, selg, scores, ncols);
 }

@@ -157,8 +157,11 @@ gsa_status gsa_prefill_tile(int32_t dtype, int32_t d, int32_t* block_m, int32_t*
  *   k_cache, v_cache  [B, Hkv, kv_len, d] (by strides), bf16
  *   lse      nullable float [B, Hq]
  *   sel      int32 [B, Hkv, 1, top_k]; sel_groups [B, Hkv, 1, l2_top_k] or NULL
- *   ws       device workspace of at least gsa_decode_workspace_bytes(); its
- *            contents need no initialisation and are clobbered.
+ *   ws       device workspace of at least gsa_decode_workspace_bytes(),
+ *            256-byte aligned.  Zero-fill it once before its first use: it
+ *            starts with per-(batch, KV head) completion counters that every
+ *            call leaves at zero again.  Calls that share one workspace must
+ *            not overlap (same stream, or serialised by the caller).
  * Requires bf16 inputs, d in {64,128}, Hq/Hkv <= 16. */
 gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
                            gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
