@@ -86,8 +86,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
     const int* __restrict__ tile_list, float c2, int fixed, int total) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned short Klds[2 * kBN * D];   // double buffered
-  __shared__ __attribute__((aligned(1024))) unsigned short Vlds[2 * kBN * D];
+  // Double-buffered K and V tiles as four separate arrays, indexed only
+  // statically (the tile loop is unrolled by two): the compiler can then tell
+  // the prefetch's LDS writes from the reads of the current tile and does not
+  // make those reads wait for the prefetch.
+  __shared__ __attribute__((aligned(1024))) unsigned short K0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) unsigned short V0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) unsigned short K1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) unsigned short V1[kBN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -150,9 +156,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     koff[it] = 8 * (sslot ^ swz_k<D>(row));
     voff[it] = 8 * (sslot ^ swz_v<D>(row));
   }
-  auto fetch = [&](int idx, int buf, int& slot, int& kind, int& u0, int& width, int& code) {
-    const int kt = list[idx];
-    code = codes[kt];
+  auto fetch = [&](int kt, unsigned short* Kd, unsigned short* Vd, int& slot, int& kind, int& u0,
+                   int& width) {
     int u1;
     slot = tile_span(l, kt, kind, u0, u1);
     width = u1 - u0;
@@ -173,10 +178,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
                             (size_t)(wave * C::NIW + it) * C::RPI * vstep;
         const unsigned klane = (unsigned)srow * kstep + 2u * (unsigned)koff[it];
         const unsigned vlane = (unsigned)srow * vstep + 2u * (unsigned)voff[it];
-        __builtin_amdgcn_global_load_lds((glb_void_ptr)(kbase + klane),
-                                         (lds_void_ptr)(Klds + buf * kBN * D + wi * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void_ptr)(vbase + vlane),
-                                         (lds_void_ptr)(Vlds + buf * kBN * D + wi * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_ptr)(kbase + klane), (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_ptr)(vbase + vlane), (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
       }
       (void)row0;
       return;
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       const int p = affine ? sm.base + (u0 + key) * sm.stride1 : map_pos(sm, u0 + key);
       const unsigned short* kp = kb + (int64_t)p * kst + koff[it];
       const unsigned short* vp = vb + (int64_t)p * vst + voff[it];
-      __builtin_amdgcn_global_load_lds((glb_void_ptr)kp, (lds_void_ptr)(Klds + buf * kBN * D + wi * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void_ptr)vp, (lds_void_ptr)(Vlds + buf * kBN * D + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)kp, (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)vp, (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
     }
   };
 
@@ -201,51 +204,88 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   const int tr_row = 4 * (tg >> 1) + (tj >> 2);
   const int tr_piece = 2 * (tg & 1) + ((tj & 3) >> 1);
   const int tr_half = tj & 1;
-  int qk_off[C::KS], tr_off[C::MT];   // loop-invariant LDS element offsets
+  // Loop-invariant LDS element offsets.  The empty asm makes each opaque, so
+  // every LDS read is one offset from its buffer and keeps that buffer's
+  // alias scope (reads reached through longer chains of derived addresses
+  // lose it and then wait for every copy in flight, the prefetch included).
+  int qk_off[C::KS], tr_off[C::MT];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) qk_off[ks] = n * D + 8 * ((h2 + 2 * ks) ^ swz_k<D>(n));
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qk_off[ks] = n * D + 8 * ((h2 + 2 * ks) ^ swz_k<D>(n));
+    asm volatile("" : "+v"(qk_off[ks]));
+  }
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
+  for (int mt = 0; mt < C::MT; ++mt) {
     tr_off[mt] = tr_row * D + 8 * ((4 * mt + tr_piece) ^ swz_v<D>(tr_row)) + 4 * tr_half;
+    asm volatile("" : "+v"(tr_off[mt]));
+  }
 
-  int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0;
-  if (cnt > 0) fetch(0, 0, nslot, nkind, nu0, nwidth, ncode);
+  // Tile ids run one tile ahead of the copies and codes one tile ahead of
+  // their use, so neither global load stalls the loop.
+  int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0, kt_next = 0;
+  if (cnt > 0) {
+    const int kt0 = list[0];
+    fetch(kt0, K0, V0, nslot, nkind, nu0, nwidth);
+    ncode = codes[kt0];
+    if (cnt > 1) kt_next = list[1];
+  }
 
-  for (int idx = 0; idx < cnt; ++idx) {
+  auto tile = [&](int idx, const unsigned short* Kb, const unsigned short* Vb, unsigned short* Kn,
+                  unsigned short* Vn) {
     const int slot = nslot, kind = nkind, u0 = nu0, width = nwidth, code = ncode;
-    const unsigned short* Kb = Klds + (idx & 1) * (kBN * D);
-    const unsigned short* Vb = Vlds + (idx & 1) * (kBN * D);
-    // One barrier per tile: this wave's loads of tile idx have landed (the
-    // barrier waits for them), and every wave is done with tile idx-1, whose
-    // buffer the next fetch overwrites.
+    // One barrier per tile: this wave's copies of tile idx have landed (the
+    // wait), so after the barrier all have, and every wave is done with tile
+    // idx - 1, whose buffers the next fetch overwrites.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (idx + 1 < cnt) fetch(idx + 1, (idx + 1) & 1, nslot, nkind, nu0, nwidth, ncode);
+    if (idx + 1 < cnt) {
+      fetch(kt_next, Kn, Vn, nslot, nkind, nu0, nwidth);
+      ncode = codes[kt_next];
+      if (idx + 2 < cnt) kt_next = list[idx + 2];
+    }
 
     // ---- S^T = K Q^T: keys 0..31 into s0 first, then keys 32..63 into s1, so
     // the softmax of the first half can start while the second half's MFMAs run.
+    // All K operands of the first half are read before its MFMA chain starts,
+    // and each second-half read is issued beside a first-half MFMA, so LDS
+    // latency overlaps the chain instead of preceding every step.
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    bf16x8 ka[C::KS], kc[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&Kb[qk_off[ks]]),
-                                                   qreg[ks], s0, 0, 0, 0);
+    for (int ks = 0; ks < C::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + qk_off[ks]);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)   // rows n and 32 + n share their swizzle
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(&Kb[qk_off[ks] + 32 * D]), qreg[ks], s1, 0, 0, 0);
+    for (int ks = 0; ks < C::KS; ++ks) {   // rows n and 32 + n share their swizzle
+      kc[ks] = *reinterpret_cast<const bf16x8*>(Kb + qk_off[ks] + 32 * D);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qreg[ks], s1, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read beside
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // each first-half MFMA
+    }
 
     // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
     if (code != 2 || width < kBN) {
+      // visibility bits first (a compact loop: this path is rare), then the mask
+      unsigned vis = 0;   // bit j: key of s0[j]; bit 16 + j: key of s1[j]
+#pragma unroll 1
+      for (int j = 0; j < 32; ++j) {
+        const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
+        bool vv = key < width;
+        if (vv && code != 2)
+          vv = key_visible(l, i, kind, u0 + key, map_pos(slot_map(l, slot), u0 + key), selrow, selgrow);
+        vis |= (unsigned)vv << j;
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key0 = 8 * (j >> 2) + 4 * h2 + (j & 3);
-        const int key1 = key0 + 32;
-        bool v0 = key0 < width, v1 = key1 < width;
-        if (code != 2) {
-          if (v0) v0 = key_visible(l, i, kind, u0 + key0, map_pos(slot_map(l, slot), u0 + key0), selrow, selgrow);
-          if (v1) v1 = key_visible(l, i, kind, u0 + key1, map_pos(slot_map(l, slot), u0 + key1), selrow, selgrow);
-        }
-        if (!v0) s0[j] = -__builtin_inff();
-        if (!v1) s1[j] = -__builtin_inff();
+        if (!((vis >> j) & 1u)) s0[j] = -__builtin_inff();
+        if (!((vis >> (16 + j)) & 1u)) s1[j] = -__builtin_inff();
       }
     }
 
@@ -253,6 +293,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16& sh = half ? s1 : s0;
+      // V^T operands of this half first: their LDS latency hides behind the
+      // softmax below.
+      s16x4 vlo[C::MT][2], vhi[C::MT][2];
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int st = 2 * half + x;   // rows 16 st + tr_row (+8) share the swizzle of tr_row
+          vlo[mt][x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st) * D));
+          vhi[mt][x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st + 8) * D));
+        }
+      }
       float mx = sh[0];
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sh[j]);
@@ -303,18 +355,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          const int st = 2 * half + x;   // rows 16 st + tr_row (+8) share the swizzle of tr_row
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st) * D));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st + 8) * D));
-          const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+          const u32x2 wl = __builtin_bit_cast(u32x2, vlo[mt][x]), wh = __builtin_bit_cast(u32x2, vhi[mt][x]);
           const u32x4 w = u32x4{wl[0], wl[1], wh[0], wh[1]};
           oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pk[x],
                                                              oacc[mt], 0, 0, 0);
         }
       }
     }
+  };
+  for (int idx = 0; idx < cnt; idx += 2) {
+    tile(idx, K0, V0, K1, V1);
+    if (idx + 1 < cnt) tile(idx + 1, K1, V1, K0, V0);
   }
 
   // ---- normalise and store: lane holds O^T[d][query n], d = 32mt + 8(j/4) + 4h2 + j%4
