@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   // re-read its last row: those keys are masked to -inf, so their P is 0 and
   // the duplicate (finite) values never count.
   const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);   // wave index as a scalar: uniform addresses stay scalar
   int koff[C::NIW], voff[C::NIW];   // element offset of the piece this lane fetches
 #pragma unroll
   for (int it = 0; it < C::NIW; ++it) {
@@ -168,25 +169,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       // load is a wave-uniform base (row block it) plus a 32-bit lane offset.
       const int p0 = sm.base + u0 * sm.stride1;
       const unsigned kstep = (unsigned)(sm.stride1 * kst) * 2u, vstep = (unsigned)(sm.stride1 * vst) * 2u;
-      const int row0 = wave * C::NIW * C::RPI + srow;
 #pragma unroll
       for (int it = 0; it < C::NIW; ++it) {
-        const int wi = wave * C::NIW + it;
+        const int wi = wv * C::NIW + it;
         const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)p0 * kst) +
-                            (size_t)(wave * C::NIW + it) * C::RPI * kstep;
+                            (size_t)wi * C::RPI * kstep;
         const char* vbase = reinterpret_cast<const char*>(vb + (int64_t)p0 * vst) +
-                            (size_t)(wave * C::NIW + it) * C::RPI * vstep;
+                            (size_t)wi * C::RPI * vstep;
         const unsigned klane = (unsigned)srow * kstep + 2u * (unsigned)koff[it];
         const unsigned vlane = (unsigned)srow * vstep + 2u * (unsigned)voff[it];
         __builtin_amdgcn_global_load_lds((glb_void_ptr)(kbase + klane), (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((glb_void_ptr)(vbase + vlane), (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
       }
-      (void)row0;
       return;
     }
 #pragma unroll
     for (int it = 0; it < C::NIW; ++it) {
-      const int wi = wave * C::NIW + it;
+      const int wi = wv * C::NIW + it;
       const int row = wi * C::RPI + srow;
       const int key = imin(row, width - 1);
       const int p = affine ? sm.base + (u0 + key) * sm.stride1 : map_pos(sm, u0 + key);
@@ -272,15 +271,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 
     // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
     if (code != 2 || width < kBN) {
-      // visibility bits first (a compact loop: this path is rare), then the mask
+      // Where no selection is involved (sinks, level-2 gists, single-level
+      // gists, raws without top-k) a row's visible keys in a tile form one
+      // range of stream indices: those at or before the query, and for raws
+      // also inside the window.  Both ends come in closed form.
+      const bool ranged = kind == K_SINK || kind == K_GIST2 || (kind == K_GIST && l.G2 == 0) ||
+                          (kind == K_RAW && l.k == 0);
+      int klo = 0, khi = width;
+      if (code != 2 && ranged) {
+        khi = iclamp(count_below(l, kind, i + 1) - u0, 0, width);
+        if (kind == K_RAW) klo = iclamp(count_below(l, K_RAW, i - l.W1 + 1) - u0, 0, width);
+      }
       unsigned vis = 0;   // bit j: key of s0[j]; bit 16 + j: key of s1[j]
+      if (code == 2 || ranged) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
+          vis |= (unsigned)(key >= klo && key < khi) << j;
+        }
+      } else {
+        // selection-dependent visibility, key by key (a compact loop)
 #pragma unroll 1
-      for (int j = 0; j < 32; ++j) {
-        const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
-        bool vv = key < width;
-        if (vv && code != 2)
-          vv = key_visible(l, i, kind, u0 + key, map_pos(slot_map(l, slot), u0 + key), selrow, selgrow);
-        vis |= (unsigned)vv << j;
+        for (int j = 0; j < 32; ++j) {
+          const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
+          bool vv = key < width;
+          if (vv) vv = key_visible(l, i, kind, u0 + key, map_pos(slot_map(l, slot), u0 + key), selrow, selgrow);
+          vis |= (unsigned)vv << j;
+        }
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
