@@ -322,48 +322,51 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
           vhi[mt][x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(Vb + tr_off[mt] + (16 * st + 8) * D));
         }
       }
-      float mx = sh[0];
+      // P = exp2(s c2 - m_run), packed to bf16 as the PV operand; the row sum
+      // adds the bf16-rounded P actually fed to the PV product, so numerator
+      // and normaliser use the same weights.  (Packed words stay in scalars:
+      // bit-casting elements of a u32x4 here made the compiler feed the first
+      // element to every dot2.)
+      bf16x8 pk[2];
+      float psum;
+      auto expo = [&]() {
+        psum = 0.f;
+        const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sh[j]);
-      {  // max with the other half-wave (same queries, the other 16 keys)
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      // Lazy rescale: the reference max m_run only moves when some row's max
-      // exceeds it by more than 8 (log2 units), so P stays <= 256, which bf16
-      // and the fp32 sums hold without loss; most steps skip the rescale.
-      const float m_tile = mx * c2;
-      if (__ballot(m_tile > m_run + 8.f)) {
-        const float m_up = fmaxf(m_run, m_tile);
+        for (int x = 0; x < 2; ++x) {
+          unsigned w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 8 * x + 2 * e;
+            w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sh[j], c2, -m_run)),
+                               __builtin_amdgcn_exp2f(fmaf(sh[j + 1], c2, -m_run)));
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, psum, false);
+          }
+          pk[x] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        }
+      };
+      // Lazy rescale without a max on the common path: P is taken against the
+      // running reference m_run straight away.  While no lane's sum exceeds
+      // 256, every P is at most 256, which bf16 and the fp32 sums hold without
+      // loss.  Otherwise (the first tile, or scores well above the reference)
+      // the row max is taken, m_run moves up to it, O and the sum are
+      // rescaled, and P is recomputed.
+      expo();
+      if (__ballot(!(psum <= 256.f))) {
+        float mx = sh[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sh[j]);
+        {  // max with the other half-wave (same queries, the other 16 keys)
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_up = fmaxf(m_run, mx * c2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_up);
         l_run *= alpha;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
         m_run = m_up;
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sh[j] = __builtin_amdgcn_exp2f(fmaf(sh[j], c2, -m_run));
-
-      // P^T operands of steps 2 half + {0,1}: accumulator regs 8 x .. 8 x + 7.
-      // The row sum adds the bf16-rounded P actually fed to the PV product, so
-      // numerator and normaliser use the same weights.  (Packed words stay in
-      // scalars: bit-casting elements of a u32x4 here made the compiler feed
-      // the first element to every dot2.)
-      bf16x8 pk[2];
-      float psum = 0.f;
-      const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int base = 8 * x;
-        const unsigned w0 = pack_bf16x2(sh[base + 0], sh[base + 1]);
-        const unsigned w1 = pack_bf16x2(sh[base + 2], sh[base + 3]);
-        const unsigned w2 = pack_bf16x2(sh[base + 4], sh[base + 5]);
-        const unsigned w3 = pack_bf16x2(sh[base + 6], sh[base + 7]);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, psum, false);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, psum, false);
-        pk[x] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+        expo();
       }
       l_run += psum;
 
