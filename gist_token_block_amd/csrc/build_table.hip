@@ -75,6 +75,44 @@ __global__ __launch_bounds__(kThreads) void k_build_table(Lay l, int q_begin, in
     if (kt < l.nkt) {
       int kind, u0, u1;
       tile_span(l, kt, kind, u0, u1);
+      // Without a selection each row sees one interval [lo_r, hi_r) of the
+      // stream; both ends are non-decreasing in r (by at most one per row), so
+      // the first and last rows decide FULL, and a tile is EMPTY unless some
+      // row reaching it has a non-empty interval.
+      const bool is_raw = kind == K_RAW;
+      const bool ranged = kind == K_SINK || kind == K_GIST2 || (kind == K_GIST && l.G2 == 0) ||
+                          (is_raw && l.k == 0);
+      if (ranged) {
+        auto hi_of = [&](const RowInfo& ri) {
+          return kind == K_SINK ? ri.sink_hi : kind == K_GIST2 ? ri.g2_hi : kind == K_GIST ? ri.g_hi : ri.r_hi;
+        };
+        const RowInfo first = rows[0], last = rows[nrows - 1];
+        const int lo_first = is_raw ? first.r_wlo : 0, lo_last = is_raw ? last.r_wlo : 0;
+        if (lo_last <= u0 && hi_of(first) >= u1) {
+          code = 2;
+        } else if (hi_of(last) <= u0 || lo_first >= u1) {
+          code = 0;
+        } else if (!is_raw) {
+          code = 1;
+        } else {
+          // rows [ra, rb) reach the tile: r_hi > u0 from ra on, r_wlo < u1 before rb
+          int a = 0, b = nrows;
+          while (a < b) {
+            const int m = (a + b) >> 1;
+            if (rows[m].r_hi > u0) b = m; else a = m + 1;
+          }
+          const int ra = a;
+          a = ra; b = nrows;
+          while (a < b) {
+            const int m = (a + b) >> 1;
+            if (rows[m].r_wlo >= u1) b = m; else a = m + 1;
+          }
+          code = 0;
+          for (int r = ra; r < a; ++r)
+            if (rows[r].r_wlo < rows[r].r_hi) { code = 1; break; }
+        }
+        table[row_base + kt] = (int8_t)code;
+      } else {
       int cnt = 0;
       for (int r = 0; r < nrows; ++r) {
         const RowInfo ri = rows[r];
@@ -109,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_build_table(Lay l, int q_begin, in
       const int area = nrows * (u1 - u0);
       code = cnt == 0 ? 0 : (cnt == area ? 2 : 1);
       table[row_base + kt] = (int8_t)code;
+      }
     }
     const int flag = code != 0;
     const unsigned long long bal = __ballot(flag);

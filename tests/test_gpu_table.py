@@ -37,6 +37,9 @@ CASES = [
     (dict(n_sink=3, chunk_len=6, gists=1, window=10, top_k=3), 3 + 50 * 7 + 2, 0, 3 + 50 * 7 + 2, 32, 16),
     (dict(n_sink=3, chunk_len=4, gists=1, window=6, top_k=3, l2_chunks=3, l2_gists=1, l2_top_k=2),
      3 + 12 * 16 + 5, 0, 3 + 12 * 16 + 5, 16, 8),
+    # window of 2 behind 3 gists: query tiles [3,4], [13,14], ... reach a raw
+    # tile only through rows whose windows hold no raw at all (EMPTY tiles)
+    (dict(n_sink=0, chunk_len=2, gists=3, window=2, top_k=0), 100, 3, 97, 2, 4),
 ]
 
 
