@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   __shared__ __attribute__((aligned(1024))) unsigned short V0[kBN * D];
   __shared__ __attribute__((aligned(1024))) unsigned short K1[kBN * D];
   __shared__ __attribute__((aligned(1024))) unsigned short V1[kBN * D];
+  // Per query row of the tile: stream entries of each kind at or before the
+  // row (index = kind), and raws before its window (index 4).  Kept here
+  // rather than in registers for the rare masking of partial tiles.
+  __shared__ int rbound[5][kBM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -127,6 +131,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       qreg[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  if (h2 == 0) {
+    const int row = wave * 32 + n;
+    rbound[K_SINK][row] = count_below(l, K_SINK, i + 1);
+    rbound[K_GIST2][row] = l.G2 ? count_below(l, K_GIST2, i + 1) : 0;
+    rbound[K_GIST][row] = count_below(l, K_GIST, i + 1);
+    rbound[K_RAW][row] = count_below(l, K_RAW, i + 1);
+    rbound[4][row] = count_below(l, K_RAW, i - l.W1 + 1);
+  }   // read only after the first tile's barrier
   const int* selrow = sel ? sel + (((size_t)b * Hkv + h) * q_len + imin(r, q_len - 1)) * l.k : nullptr;
   const int* selgrow = selg ? selg + (((size_t)b * Hkv + h) * q_len + imin(r, q_len - 1)) * l.k2 : nullptr;
 
@@ -246,16 +258,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     // ---- S^T = K Q^T: keys 0..31 into s0 first, then keys 32..63 into s1, so
     // the softmax of the first half can start while the second half's MFMAs run.
     // All K operands of the first half are read before its MFMA chain starts,
-    // and each second-half read is issued beside a first-half MFMA, so LDS
-    // latency overlaps the chain instead of preceding every step.
+    // and each second-half read is issued right after a first-half MFMA, so
+    // LDS latency overlaps the chain instead of preceding every step.
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     bf16x8 ka[C::KS], kc[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(Kb + qk_off[ks]);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {   // rows n and 32 + n share their swizzle
-      kc[ks] = *reinterpret_cast<const bf16x8*>(Kb + qk_off[ks] + 32 * D);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[ks], s0, 0, 0, 0);
+      kc[ks] = *reinterpret_cast<const bf16x8*>(Kb + qk_off[ks] + 32 * D);
     }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[ks], qreg[ks], s1, 0, 0, 0);
@@ -265,8 +277,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // an LDS read beside
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // each first-half MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // each first-half MFMA, then
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // a second-half read (it may reuse the MFMA's operand registers)
     }
 
     // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
@@ -279,8 +291,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
                           (kind == K_RAW && l.k == 0);
       int klo = 0, khi = width;
       if (code != 2 && ranged) {
-        khi = iclamp(count_below(l, kind, i + 1) - u0, 0, width);
-        if (kind == K_RAW) klo = iclamp(count_below(l, K_RAW, i - l.W1 + 1) - u0, 0, width);
+        const int row = wave * 32 + n;
+        khi = iclamp(rbound[kind][row] - u0, 0, width);
+        if (kind == K_RAW) klo = iclamp(rbound[4][row] - u0, 0, width);
       }
       unsigned vis = 0;   // bit j: key of s0[j]; bit 16 + j: key of s1[j]
       if (code == 2 || ranged) {
