@@ -236,7 +236,7 @@ def run_decode(w, args, torch, gsa, copies=4):
             "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "unique_bytes": nbytes,
             "visible_rows_per_group": round(float(rows) / (w.batch * w.hkv), 2),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernels": "score_select + decode_split + decode_combine", "cache_copies": copies}
+            "kernels": "score_select + decode", "cache_copies": copies}
 
 
 def profile_pass(torch, gsa, args):
