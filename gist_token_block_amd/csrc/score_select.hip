@@ -30,11 +30,35 @@ __device__ inline bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
+// Value of lane ^ j for a constant j (the networks below unroll fully):
+// DPP quad permutes for 1 and 2, a row rotation by 8 for 8 (a rotation by half
+// a 16-lane row is the xor), a swizzle for 4, and the row / half swaps for 16
+// and 32, instead of an LDS permute.  The swaps exchange the two rows (or
+// halves) of their operands, so the partner's value is the second result in
+// the lower row or half and the first in the upper.
+__device__ inline int xor_lane(int v, int j) {
+  const int lane = __lane_id();
+  if (j == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if (j == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if (j == 8) return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  if (j == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101F);                      // xor 4 in 32-lane groups
+  if (j == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((lane & 16) ? sw[0] : sw[1]);
+  }
+  if (j == 32) {
+    const auto sw = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((lane & 32) ? sw[0] : sw[1]);
+  }
+  return __shfl_xor(v, j);
+}
+__device__ inline float xor_lane(float v, int j) { return __int_as_float(xor_lane(__float_as_int(v), j)); }
+
 // One compare-exchange stage of a 64-lane bitonic network: the lane keeps the
 // better of (own, partner at lane ^ j) if keep_better, else the worse.
 __device__ inline void cx(float& s, int& id, int j, bool keep_better) {
-  const float os = __shfl_xor(s, j);
-  const int oi = __shfl_xor(id, j);
+  const float os = xor_lane(s, j);
+  const int oi = xor_lane(id, j);
   if (better(os, oi, s, id) == keep_better) {
     s = os;
     id = oi;
@@ -74,7 +98,7 @@ __device__ inline void wave_sort_int_asc(int& v) {
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const int o = __shfl_xor(v, j);
+      const int o = xor_lane(v, j);
       const bool up = (lane & k) == 0;
       const bool lower = (lane & j) == 0;
       const bool keep_small = lower == up;
@@ -194,7 +218,7 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
     for (int it = 0; it < ITER; ++it) {
       float v = part[it];
 #pragma unroll
-      for (int j = 1; j < LPR; j <<= 1) v += __shfl_xor(v, j);
+      for (int j = 1; j < LPR; j <<= 1) v += xor_lane(v, j);
       if (sub == it) mine = v;
     }
     const int e = bi * 64 + grp + RPI * sub;
