@@ -180,3 +180,43 @@ def test_decode_small_layouts(case):
         assert_close(o.cpu().numpy(), ref[:, 0], TOL["bf16"], what="fixed-layout decode")
         return
     _check_decode(layout, rng_q, kc, vc, L, 1 / math.sqrt(d))
+
+
+@pytest.mark.parametrize("w", [configs.SELECTIVE_DECODE, configs.HIER_DECODE], ids=lambda w: w.name)
+def test_decode_workspace_reuse_and_graph_replay(w):
+    """One workspace across many calls: the completion counters must come back
+    to zero after every call, so repeated calls (eager, then replays of a
+    captured graph with eager work between them) give bit-identical outputs."""
+    x = inputs.decode_inputs(w, seed=5)
+    L = w.seq_len
+    tq, tk, tv = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
+    scale = 1 / math.sqrt(w.d)
+    sel, selg, _ = gsa.score_select(w.layout, tq, tk, L, L - 1, scale, cache_layout=True)
+    need = gsa.decode_workspace_bytes(w.layout, w.batch, w.hq, w.hkv, w.d, L)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    o = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=dev())
+    lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device=dev())
+    gsa.attn_decode(w.layout, tq, tk, tv, sel, selg, scale, workspace=ws, out=(o, lse))
+    torch.cuda.synchronize()
+    ref_o, ref_lse = o.clone(), lse.clone()
+    n_counters = w.batch * w.hkv
+    for _ in range(3):
+        o.zero_()
+        gsa.attn_decode(w.layout, tq, tk, tv, sel, selg, scale, workspace=ws, out=(o, lse))
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+        assert int(ws[:4 * n_counters].view(torch.int32).abs().sum()) == 0, "counters not reset"
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            gsa.attn_decode(w.layout, tq, tk, tv, sel, selg, scale, workspace=ws, out=(o, lse))
+    torch.cuda.current_stream().wait_stream(st)
+    for _ in range(3):
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+        assert int(ws[:4 * n_counters].view(torch.int32).abs().sum()) == 0, "counters not reset"
