@@ -31,7 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 64;          // rows per staged block (double buffered)
 constexpr int kMaxSeg = 3 + 64 + 64;
-constexpr int kMaxSplit = 64;      // splits per (batch, KV head) the merge step holds
+constexpr int kMaxSplit = 64;      // most splits per (batch, KV head)
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* glb_void_ptr;
@@ -277,7 +277,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   float* cl = wstat + 4 * 16;                          // [4][16]
   float* co = reinterpret_cast<float*>(stage);         // [4][16][D]
   static_assert(2 * kRows * D * 2 >= 64 * D * 4, "LDS reuse too small");
-  static_assert(2 * kRows * D * 2 >= (2 * kMaxSplit * 16 + 32) * 4, "LDS reuse too small");
   if (grp == 0) {
     cm[wave * 16 + col] = m_run;
     cl[wave * 16 + col] = l_run;
@@ -320,49 +319,46 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   __syncthreads();
   if (!am_last) return;
   const float* gp = part + gidx * nsplit * G * (D + 2);
-  // (max, sum) of every split and head in one parallel load, then the weights
-  float* sm = reinterpret_cast<float*>(stage);       // [nsplit][G] maxima, then weights
-  float* sl = sm + kMaxSplit * 16;                   // [nsplit][G] sums
-  float* hm = sl + kMaxSplit * 16;                   // [G] merged max, [G] merged sum
-  for (int x = tid; x < nsplit * G; x += kThreads) {
-    const float* pp = gp + x * (D + 2);
-    sm[x] = ld_dev(&pp[D]);
-    sl[x] = ld_dev(&pp[D + 1]);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = kNegBig;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, sm[sp * G + tid]);
-    float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) L += sl[sp * G + tid] * __builtin_amdgcn_exp2f(sm[sp * G + tid] - M);
-    hm[tid] = M;
-    hm[16 + tid] = L;
-  }
-  __syncthreads();
-  for (int x = tid; x < nsplit * G; x += kThreads) sm[x] = __builtin_amdgcn_exp2f(sm[x] - hm[x % G]);
-  __syncthreads();
+  // Each thread merges one (head, d) over all splits, loading every split's
+  // partial, max and sum of a batch together (one round trip per 16 splits)
+  // and rescaling online between batches.
   for (int x = tid; x < G * D; x += kThreads) {
     const int hd = x / D, dd = x - hd * D;
-    float O = 0.f;
+    float Mr = kNegBig, Lr = 0.f, Or = 0.f;
     for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-      float po[16];
+      float po[16], pm[16], pl[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {   // all loads of the batch in flight together
-        const int sp = imin(sp0 + j, nsplit - 1);
-        po[j] = ld_dev(&gp[(sp * G + hd) * (D + 2) + dd]);
+        const float* pp = gp + (imin(sp0 + j, nsplit - 1) * G + hd) * (D + 2);
+        po[j] = ld_dev(&pp[dd]);
+        pm[j] = ld_dev(&pp[D]);
+        pl[j] = ld_dev(&pp[D + 1]);
       }
+      float mb = Mr;
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (sp0 + j < nsplit) O += po[j] * sm[(sp0 + j) * G + hd];
+        if (sp0 + j < nsplit) mb = fmaxf(mb, pm[j]);
+      const float a = __builtin_amdgcn_exp2f(Mr - mb);
+      Lr *= a;
+      Or *= a;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (sp0 + j < nsplit) {
+          const float wgt = __builtin_amdgcn_exp2f(pm[j] - mb);
+          Lr = fmaf(pl[j], wgt, Lr);
+          Or = fmaf(po[j], wgt, Or);
+        }
+      }
+      Mr = mb;
     }
-    const float val = O / hm[16 + hd];
+    const float val = Or / Lr;
     TO* orow = o + b * osb + (int64_t)(h * G + hd) * osh;
     if constexpr (sizeof(TO) == 4) {
       orow[dd] = val;
     } else {
       orow[dd] = (TO)(pack_bf16x2(val, 0.f) & 0xffffu);
     }
-    if (lse && dd == 0) lse[(size_t)b * Hq + h * G + hd] = (hm[hd] + __log2f(hm[16 + hd])) * kLn2;
+    if (lse && dd == 0) lse[(size_t)b * Hq + h * G + hd] = (Mr + __log2f(Lr)) * kLn2;
   }
   if (tid == 0) __hip_atomic_store(&counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
