@@ -92,19 +92,26 @@ __device__ inline void wave_merge(float& rs, int& ri, float xs, int xi) {
   for (int j = 32; j > 0; j >>= 1) cx(rs, ri, j, (lane & j) == 0);
 }
 
-__device__ inline void wave_sort_int_asc(int& v) {
+// Lanes [0, k) of a best-first list hold the chosen ids, INT_MAX where fewer
+// than k were chosen; being the worst entries, those fill lanes [nv, k).
+// Write the ids ascending into out[0, k), -1 padded: each lane counts the
+// chosen ids smaller than its own (ids are distinct), so no sorting network
+// is needed.  kept (if given, 64 entries) receives the same list, INT_MAX
+// padded.  Returns the number chosen.
+__device__ inline int place_ascending(int v, int k, int* __restrict__ out, int* kept) {
   const int lane = __lane_id();
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int o = xor_lane(v, j);
-      const bool up = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool keep_small = lower == up;
-      if ((o < v) == keep_small && o != v) v = o;
-    }
+  const bool valid = lane < k && v != INT_MAX;
+  const int nv = __popcll(__ballot(valid));
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += (__builtin_amdgcn_readlane(v, j) < v) ? 1 : 0;
+  if (valid) {
+    out[rank] = v;   // rank < nv
+    if (kept) kept[rank] = v;
+  } else {
+    if (lane < k) out[lane] = -1;   // lane >= nv
+    if (kept) kept[lane] = INT_MAX;
   }
+  return nv;
 }
 
 template <typename T> struct Vec16;
@@ -177,6 +184,7 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
   ri = INT_MAX;
   const int nbatch = (ncand + 63) / 64;
   const int ng = cands.ngist();
+  bool empty = true;   // running list still all -inf: the first sorted batch becomes it
   for (int bi = wave; bi < nbatch; bi += nw) {
     float part[ITER];
     if (ITER <= 16 && ng == 1) {
@@ -230,7 +238,13 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
       if (score_out) score_out[id] = s;
     }
     wave_sort_best_first(s, id);
-    wave_merge(rs, ri, s, id);
+    if (empty) {
+      rs = s;
+      ri = id;
+      empty = false;
+    } else {
+      wave_merge(rs, ri, s, id);
+    }
   }
   // merge tree: at step st, wave w (w % 2st == 0) absorbs wave w + st
   lds_s[wave * 64 + lane] = rs;
@@ -279,11 +293,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_score_select(
       for (int e = ncand + tid; e < ncols; e += nthr) so[e] = -__builtin_inff();
     ChunkCands cands{&l};
     score_and_rank<T, D>(kb, kst, qbar, ncand, scale / (float)l.g, cands, so, lds_s, lds_i, rs, ri);
-    if (wave == 0) {
-      int v = (lane < l.k && ri != INT_MAX) ? ri : INT_MAX;
-      wave_sort_int_asc(v);
-      if (lane < l.k) sel[row * l.k + lane] = v == INT_MAX ? -1 : v;
-    }
+    if (wave == 0) place_ascending(lane < l.k ? ri : INT_MAX, l.k, sel + row * l.k, nullptr);
     return;
   }
 
@@ -296,22 +306,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_score_select(
   score_and_rank<T, D>(kb, kst, qbar, ng2, scale / (float)l.g2, gc, so, lds_s, lds_i, rs, ri);
   __shared__ int nkept;
   if (wave == 0) {
-    int v = (lane < l.k2 && ri != INT_MAX) ? ri : INT_MAX;
-    wave_sort_int_asc(v);
-    if (lane < l.k2) selg[row * l.k2 + lane] = v == INT_MAX ? -1 : v;
-    kept[lane] = v;
-    const unsigned long long bal = __ballot(v != INT_MAX);
-    if (lane == 0) nkept = __popcll(bal);
+    const int nv = place_ascending(lane < l.k2 ? ri : INT_MAX, l.k2, selg + row * l.k2, kept);
+    if (lane == 0) nkept = nv;
   }
   __syncthreads();
   // level 1: chunks of the kept groups
   InGroupCands ic{&l, kept};
   score_and_rank<T, D>(kb, kst, qbar, nkept * l.G2, scale / (float)l.g, ic, nullptr, lds_s, lds_i, rs, ri);
-  if (wave == 0) {
-    int v = (lane < l.k && ri != INT_MAX) ? ri : INT_MAX;
-    wave_sort_int_asc(v);
-    if (lane < l.k) sel[row * l.k + lane] = v == INT_MAX ? -1 : v;
-  }
+  if (wave == 0) place_ascending(lane < l.k ? ri : INT_MAX, l.k, sel + row * l.k, nullptr);
 }
 
 template <typename T, int D>
