@@ -1,9 +1,22 @@
+import importlib.util
 import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+# Mutation testing of the oracle (tests/test_oracle_mutations.py): a child
+# pytest process gets a planted-mistake copy of the oracle through this
+# variable and must then fail its pins.  Never set in ordinary runs.
+_MUTANT = os.environ.get("GSA_ORACLE_MUTANT")
+if _MUTANT:
+    import oracle  # noqa: E402  (the package; its module is replaced below)
+    _spec = importlib.util.spec_from_file_location("oracle.gsa_oracle", _MUTANT)
+    _mod = importlib.util.module_from_spec(_spec)
+    sys.modules["oracle.gsa_oracle"] = _mod
+    _spec.loader.exec_module(_mod)
+    oracle.gsa_oracle = _mod
 
 
 def pytest_configure(config):
