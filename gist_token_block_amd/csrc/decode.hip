@@ -73,7 +73,10 @@ __device__ inline int seg_pos(const Lay& l, const Segs& s, int v) {
 }
 
 // Workspace: int counters [B*Hkv] (zero between calls), then partials
-// [B*Hkv][nsplit][G][D + 2] (O, then max in log2 units, then sum).
+// [B*Hkv][nsplit][G][D + 3] (O, then max in log2 units, then the sum of the
+// bf16 P that O is built from, then the sum of the unrounded P, which gives
+// the log-sum-exp).
+constexpr int kPartExtra = 3;
 template <int D, typename TO>
 __global__ __launch_bounds__(kThreads) void k_decode(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qsh,
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   __shared__ int rowpos[2][kRows];
   __shared__ int ssel[64], sselg[64];
   __shared__ int am_last;
-  __shared__ float wstat[128];
+  __shared__ float wstat[192];
   // Two staging buffers, K then V rows of one block each.  They are separate
   // arrays indexed only statically: the compiler can then tell the prefetch's
   // LDS writes from the reads of the current block and does not make every
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   f32x4 oacc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegBig, l_run = 0.f;
+  float m_run = kNegBig, l_run = 0.f, l_ex = 0.f;
 
   auto step = [&](int blk, const unsigned short* Kb, unsigned short* next) {
     // One barrier per block: this wave's copies of block blk have landed
@@ -251,12 +254,17 @@ __global__ __launch_bounds__(kThreads) void k_decode(
     const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
     float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.f, false);
     ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, ps, false);
+    float pe = (s[0] + s[1]) + (s[2] + s[3]);
     ps += __shfl_xor(ps, 16);
+    pe += __shfl_xor(pe, 16);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
       ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(pe), false, false);
+      pe = __uint_as_float(se[0]) + __uint_as_float(se[1]);
     }
     l_run = l_run * alpha + ps;
+    l_ex = l_ex * alpha + pe;
     m_run = m_new;
     const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
 #pragma unroll
@@ -275,34 +283,39 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   // ---- merge the 4 waves' partials, write this split's partial
   float* cm = wstat;                                   // [4][16]
   float* cl = wstat + 4 * 16;                          // [4][16]
+  float* ce = wstat + 8 * 16;                          // [4][16]
   float* co = reinterpret_cast<float*>(stage);         // [4][16][D]
   static_assert(2 * kRows * D * 2 >= 64 * D * 4, "LDS reuse too small");
   if (grp == 0) {
     cm[wave * 16 + col] = m_run;
     cl[wave * 16 + col] = l_run;
+    ce[wave * 16 + col] = l_ex;
   }
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) co[(wave * 16 + col) * D + 16 * mt + 4 * grp + e] = oacc[mt][e];
   __syncthreads();
-  float* mypart = part + (gidx * nsplit + split) * G * (D + 2);
+  constexpr int PS = D + kPartExtra;   // floats per (split, head) partial
+  float* mypart = part + (gidx * nsplit + split) * G * PS;
   for (int x = tid; x < G * D; x += kThreads) {
     const int hd = x / D, dd = x - hd * D;
     float M = kNegBig;
     for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * 16 + hd]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f, LE = 0.f, O = 0.f;
     for (int w = 0; w < 4; ++w) {
       const float f = __builtin_amdgcn_exp2f(cm[w * 16 + hd] - M);
       L += cl[w * 16 + hd] * f;
+      LE += ce[w * 16 + hd] * f;
       O += co[(w * 16 + hd) * D + dd] * f;
     }
     // device-scope stores: coherent across the XCDs' L2s without a cache-wide
     // write-back (a device-scope fence here costs far more than the kernel)
-    st_dev(&mypart[hd * (D + 2) + dd], O);
+    st_dev(&mypart[hd * PS + dd], O);
     if (dd == 0) {
-      st_dev(&mypart[hd * (D + 2) + D], M);
-      st_dev(&mypart[hd * (D + 2) + D + 1], L);
+      st_dev(&mypart[hd * PS + D], M);
+      st_dev(&mypart[hd * PS + D + 1], L);
+      st_dev(&mypart[hd * PS + D + 2], LE);
     }
   }
 
@@ -318,21 +331,22 @@ __global__ __launch_bounds__(kThreads) void k_decode(
   }
   __syncthreads();
   if (!am_last) return;
-  const float* gp = part + gidx * nsplit * G * (D + 2);
+  const float* gp = part + gidx * nsplit * G * PS;
   // Each thread merges one (head, d) over all splits, loading every split's
   // partial, max and sum of a batch together (one round trip per 16 splits)
   // and rescaling online between batches.
   for (int x = tid; x < G * D; x += kThreads) {
     const int hd = x / D, dd = x - hd * D;
-    float Mr = kNegBig, Lr = 0.f, Or = 0.f;
+    float Mr = kNegBig, Lr = 0.f, LEr = 0.f, Or = 0.f;
     for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-      float po[16], pm[16], pl[16];
+      float po[16], pm[16], pl[16], pe[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {   // all loads of the batch in flight together
-        const float* pp = gp + (imin(sp0 + j, nsplit - 1) * G + hd) * (D + 2);
+        const float* pp = gp + (imin(sp0 + j, nsplit - 1) * G + hd) * PS;
         po[j] = ld_dev(&pp[dd]);
         pm[j] = ld_dev(&pp[D]);
         pl[j] = ld_dev(&pp[D + 1]);
+        pe[j] = lse && dd == 0 ? ld_dev(&pp[D + 2]) : 0.f;
       }
       float mb = Mr;
 #pragma unroll
@@ -340,12 +354,14 @@ __global__ __launch_bounds__(kThreads) void k_decode(
         if (sp0 + j < nsplit) mb = fmaxf(mb, pm[j]);
       const float a = __builtin_amdgcn_exp2f(Mr - mb);
       Lr *= a;
+      LEr *= a;
       Or *= a;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if (sp0 + j < nsplit) {
           const float wgt = __builtin_amdgcn_exp2f(pm[j] - mb);
           Lr = fmaf(pl[j], wgt, Lr);
+          LEr = fmaf(pe[j], wgt, LEr);
           Or = fmaf(po[j], wgt, Or);
         }
       }
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(
     } else {
       orow[dd] = (TO)(pack_bf16x2(val, 0.f) & 0xffffu);
     }
-    if (lse && dd == 0) lse[(size_t)b * Hq + h * G + hd] = (Mr + __log2f(Lr)) * kLn2;
+    if (lse && dd == 0) lse[(size_t)b * Hq + h * G + hd] = (Mr + __log2f(LEr)) * kLn2;
   }
   if (tid == 0) __hip_atomic_store(&counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -378,12 +394,10 @@ size_t counters_bytes(int B, int Hkv) { return ((size_t)B * Hkv * sizeof(int) + 
 // Splits per (batch, KV head): enough workgroups for about two per CU in total,
 // each streaming a long run of 64-row blocks.
 int plan_splits(int B, int Hkv, int rows, int* rows_per_split) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-  }
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
   const int groups = imax(1, B * Hkv);
   int ns = iclamp((2 * cus + groups - 1) / groups, 1, kMaxSplit);
   ns = imin(ns, imax(1, (rows + kRows - 1) / kRows));
@@ -403,7 +417,7 @@ extern "C" size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B
   if (make_lay(layout, kv_len, 64, &l) != GSA_OK || kv_len < 1 || Hkv < 1 || Hq % Hkv) return 0;
   int rps;
   const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
-  return counters_bytes(B, Hkv) + (size_t)B * Hkv * ns * (Hq / Hkv) * (d + 2) * sizeof(float);
+  return counters_bytes(B, Hkv) + (size_t)B * Hkv * ns * (Hq / Hkv) * (d + kPartExtra) * sizeof(float);
 }
 
 extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,

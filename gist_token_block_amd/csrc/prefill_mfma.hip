@@ -76,7 +76,9 @@ template <> struct OutStore<unsigned short> {
   }
 };
 
-template <int D, typename TO>
+// LSE: also write the log-sum-exp, normalised by a separate fp32 sum of the
+// unrounded probabilities (O keeps the sum of the bf16 P that feeds it).
+template <int D, typename TO, bool LSE>
 __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
+  float l_ex = 0.f;   // LSE only: sum of the unrounded P
 
   // Staging: wave load `wi` (0 .. 4*NIW-1) fills key rows [wi*RPI, wi*RPI+RPI)
   // of a tile; lane -> row wi*RPI + lane / PPR, LDS slot lane % PPR, which
@@ -341,9 +344,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       // bit-casting elements of a u32x4 here made the compiler feed the first
       // element to every dot2.)
       bf16x8 pk[2];
-      float psum;
+      float psum, pex;
       auto expo = [&]() {
         psum = 0.f;
+        pex = 0.f;
         const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -351,9 +355,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 8 * x + 2 * e;
-            w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sh[j], c2, -m_run)),
-                               __builtin_amdgcn_exp2f(fmaf(sh[j + 1], c2, -m_run)));
+            const float pa = __builtin_amdgcn_exp2f(fmaf(sh[j], c2, -m_run));
+            const float pb = __builtin_amdgcn_exp2f(fmaf(sh[j + 1], c2, -m_run));
+            w[e] = pack_bf16x2(pa, pb);
             psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, psum, false);
+            if constexpr (LSE) pex += pa + pb;
           }
           pk[x] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
         }
@@ -376,12 +382,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
         const float m_up = fmaxf(m_run, mx * c2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_up);
         l_run *= alpha;
+        if constexpr (LSE) l_ex *= alpha;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt) oacc[mt] *= alpha;
         m_run = m_up;
         expo();
       }
       l_run += psum;
+      if constexpr (LSE) l_ex += pex;
 
       // O^T += V^T P^T; operand element e <-> key 16 st + 8(e/4) + 4 h2 + e%4
 #pragma unroll
@@ -415,7 +423,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
                            oacc[mt][4 * jj + 2] * inv, oacc[mt][4 * jj + 3] * inv);
       }
     }
-    if (lse && h2 == 0) lse[((size_t)b * Hq + hq) * q_len + r] = (m_run + __log2f(l_tot)) * kLn2;
+    if constexpr (LSE) {
+      const float l_ex_tot = l_ex + __shfl_xor(l_ex, 32);
+      if (h2 == 0) lse[((size_t)b * Hq + hq) * q_len + r] = (m_run + __log2f(l_ex_tot)) * kLn2;
+    }
   }
 }
 
@@ -463,13 +474,16 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
     const long long total = (long long)B * Hkv * nqt * (Hq / Hkv);
     if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
     const float c2 = scale * kLog2e;
-#define GSA_MFMA(D, TO)                                                                              \
-  hipLaunchKernelGGL((k_prefill_mfma<D, TO>), dim3((unsigned)total), dim3(kThreads), 0, s, l,         \
+#define GSA_MFMA1(D, TO, LSE)                                                                        \
+  hipLaunchKernelGGL((k_prefill_mfma<D, TO, LSE>), dim3((unsigned)total), dim3(kThreads), 0, s, l,    \
                      (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                \
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr,    \
                      o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, nqt, sel,      \
                      sel_groups, table, tile_cnt, tile_list, c2, (int)fixed, (int)total)
+#define GSA_MFMA(D, TO)             \
+  if (lse) GSA_MFMA1(D, TO, true);  \
+  else GSA_MFMA1(D, TO, false)
     if (d == 128) {
       if (o.dtype == GSA_F32) GSA_MFMA(128, float);
       else GSA_MFMA(128, unsigned short);
@@ -478,6 +492,7 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
       else GSA_MFMA(64, unsigned short);
     }
 #undef GSA_MFMA
+#undef GSA_MFMA1
     return launch_status("gsa_attn_prefill (mfma)");
   }
   if (block_n > 256) return fail(GSA_EUNSUPPORTED, "block_n %d > 256 on the row-wave path", block_n);

@@ -95,15 +95,22 @@ __device__ inline void wave_merge(float& rs, int& ri, float xs, int xi) {
 // Lanes [0, k) of a best-first list hold the chosen ids, INT_MAX where fewer
 // than k were chosen; being the worst entries, those fill lanes [nv, k).
 // Write the ids ascending into out[0, k), -1 padded: each lane counts the
-// chosen ids smaller than its own (ids are distinct), so no sorting network
-// is needed.  kept (if given, 64 entries) receives the same list, INT_MAX
-// padded.  Returns the number chosen.
+// chosen ids smaller than its own, and equal ones in lower lanes, so no
+// sorting network is needed and the ranks of the nv chosen lanes are always
+// a permutation of [0, nv): every slot is written even if an id repeated.
+// kept (if given, 64 entries) receives the same list, INT_MAX padded.
+// Returns the number chosen.
 __device__ inline int place_ascending(int v, int k, int* __restrict__ out, int* kept) {
   const int lane = __lane_id();
   const bool valid = lane < k && v != INT_MAX;
-  const int nv = __popcll(__ballot(valid));
+  const unsigned long long vmask = __ballot(valid);
+  const int nv = __popcll(vmask);
   int rank = 0;
-  for (int j = 0; j < k; ++j) rank += (__builtin_amdgcn_readlane(v, j) < v) ? 1 : 0;
+  for (int j = 0; j < k; ++j) {
+    const int vj = __builtin_amdgcn_readlane(v, j);
+    const bool vj_valid = (vmask >> j) & 1ull;
+    rank += (vj_valid && (vj < v || (vj == v && j < lane))) ? 1 : 0;
+  }
   if (valid) {
     out[rank] = v;   // rank < nv
     if (kept) kept[rank] = v;
@@ -157,7 +164,10 @@ struct GroupCands {        // two levels, level 2: group e
 struct InGroupCands {      // two levels, level 1: chunks of the kept groups
   const Lay* l;
   const int* groups;       // LDS, ascending
-  __device__ int chunk(int e) const { return groups[e / l->G2] * l->G2 + e % l->G2; }
+  int ngroups;              // groups complete before the query (ids are clamped into range)
+  __device__ int chunk(int e) const {
+    return iclamp(groups[e / l->G2], 0, ngroups - 1) * l->G2 + e % l->G2;
+  }
   __device__ int ngist() const { return l->g; }
   __device__ int pos(int e, int t) const { return pos_of(*l, K_GIST, chunk(e) * l->g + t); }
   __device__ int id(int e) const { return chunk(e); }
@@ -236,6 +246,10 @@ __device__ void score_and_rank(const T* __restrict__ kb, int64_t kst, const floa
       s = mine * mul;
       id = cands.id(e);
       if (score_out) score_out[id] = s;
+      // A NaN score (a NaN in a key or the query) would break the total order
+      // the networks rely on; it ranks as -inf instead.  Tested on the bits:
+      // the build assumes no NaNs, so a float comparison would be folded away.
+      if ((__float_as_uint(s) & 0x7fffffffu) > 0x7f800000u) s = -__builtin_inff();
     }
     wave_sort_best_first(s, id);
     if (empty) {
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_score_select(
   }
   __syncthreads();
   // level 1: chunks of the kept groups
-  InGroupCands ic{&l, kept};
+  InGroupCands ic{&l, kept, imax(ng2, 1)};
   score_and_rank<T, D>(kb, kst, qbar, nkept * l.G2, scale / (float)l.g, ic, nullptr, lds_s, lds_i, rs, ri);
   if (wave == 0) place_ascending(lane < l.k ? ri : INT_MAX, l.k, sel + row * l.k, nullptr);
 }

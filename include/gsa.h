@@ -130,10 +130,16 @@ gsa_status gsa_score_select(const gsa_layout* layout, gsa_tensor q, gsa_tensor k
 int32_t gsa_score_columns(const gsa_layout* layout, int32_t seq_len);
 
 /* Block-sparse prefill: softmax attention of every query row over its visible
- * keys, skipping EMPTY tiles and masking only PARTIAL ones.
+ * keys -- sinks, every earlier gist and the local window (UniGist summary,
+ * Approach), plus the raw tokens of the unfolded chunks (SSA abstract) and,
+ * with two levels, the level-1 gists of the kept groups (GSA abstract) --
+ * skipping EMPTY tiles and masking only PARTIAL ones (UniGist's summary gives
+ * skipping invisible blocks as the aim of moving its gists, Approach).
  *   q, o     [B, q_len, Hq, d]; k, v [B, seq_len, Hkv, d] (by strides)
  *   o        dtype F32, or the input dtype
- *   lse      nullable float [B, Hq, q_len], natural-log log-sum-exp
+ *   lse      nullable float [B, Hq, q_len], natural-log log-sum-exp (from an
+ *            fp32 sum of the unrounded probabilities; a bf16-input O is
+ *            normalised by the sum of the bf16 probabilities it is built from)
  *   sel, sel_groups  as produced by gsa_score_select (NULL for the fixed layout)
  *   table, tile_cnt, tile_list  from gsa_build_layout with the same block_m,
  *            block_n, q_begin, q_len (n_tables = 1 for the fixed layout, else B*Hkv)
@@ -152,7 +158,11 @@ gsa_status gsa_prefill_tile(int32_t dtype, int32_t d, int32_t* block_m, int32_t*
 /* Split-K decode: one query per sequence at position kv_len - 1 (the caller has
  * already appended that token's K and V to the cache), attending to the sinks,
  * every gist earlier than the window (two levels: every level-2 gist and the
- * level-1 gists of the kept groups), the window and the unfolded chunks.
+ * level-1 gists of the kept groups), the window and the unfolded chunks
+ * (decoding with selective unfolding: SSA abstract; gist of gist: GSA
+ * abstract; sink + gist + window: UniGist summary, Approach).
+ * The log-sum-exp is formed from an fp32 sum of the unrounded probabilities;
+ * O is normalised by the sum of the bf16 probabilities it is built from.
  *   q, o     [B, Hq, d] (stride_t unused)
  *   k_cache, v_cache  [B, Hkv, kv_len, d] (by strides), bf16
  *   lse      nullable float [B, Hq]

@@ -99,3 +99,58 @@ def test_decode_workloads_full(w):
     hits = np.mean([len(set(sel[b, h, 0]) & set(x["plant_chunks"][b]))
                     for b in range(w.batch) for h in range(w.hkv)])
     assert hits > 4   # the planted chunks are found (statistical sanity)
+
+
+def test_nan_gist_keys_rank_last():
+    """A NaN gist key gives its chunk a NaN score, which ranks below every
+    finite one (as -inf): the chosen ids stay distinct candidates, ascending,
+    and equal the top-k of the finite candidates, topped up with the NaN ones
+    (lowest ids first) where there are too few."""
+    layout = dict(n_sink=2, chunk_len=4, gists=1, window=4, top_k=4)
+    L = 2 + 40 * 5 + 1
+    lay = O.Layout.of(layout)
+    tm = O.type_map(lay, L)
+    q, k, _ = inputs.random_qkv(1, L, 4, 2, 128, seed=21, dtype="bf16")
+    nan_chunks = {1, 3, 17}
+    for m in nan_chunks:
+        k[0, tm.chunk_gists[m][0], :, :] = np.nan
+    scale = 1 / np.sqrt(128)
+    sel, _, _ = _run(layout, q, k, L, 0, scale, "bf16")
+    for h in range(2):
+        for i in range(L):
+            cands = O.chunk_candidates(lay, tm, i)
+            finite = [m for m in cands if m not in nan_chunks]
+            s = O.gist_scores(q[0, i, 2 * h:2 * h + 2], k[0, :, h], tm.chunk_gists, finite, scale)
+            chosen, gap = O.top_k(s, 4)
+            fill = sorted(m for m in cands if m in nan_chunks)[:4 - len(chosen)]
+            want = sorted(chosen + fill) + [-1] * (4 - len(chosen) - len(fill))
+            got = sel[0, h, i].tolist()
+            if got != want:
+                assert gap < 1e-3, f"row {i} head {h}: gpu {got} want {want} (gap {gap:.2e})"
+                picked = [x for x in got if x >= 0]
+                assert len(set(picked)) == len(picked) and set(picked) <= set(cands)
+
+
+def test_two_level_exact_ties_break_to_lowest_ids():
+    """Ternary inputs with a power-of-two scale make every score exact in fp32,
+    so ties are real at both levels: kept groups and unfolded chunks must equal
+    the oracle's exactly (lowest ids win), with no near-tie allowance."""
+    layout = dict(n_sink=1, chunk_len=2, gists=1, window=3, top_k=5, l2_chunks=4, l2_gists=1,
+                  l2_top_k=3)
+    P2 = 4 * 3 + 1
+    L = 1 + 40 * P2 + 2
+    lay = O.Layout.of(layout)
+    tm = O.type_map(lay, L)
+    q, k, _ = inputs.ternary_qkv(2, L, 4, 2, 64, seed=13)
+    rows = list(range(L - 6, L))
+    qb = rows[0]
+    sel, selg, _ = _run(layout, q[:, qb:], k, L, qb, 0.125, "bf16")
+    ref = O.select(lay, tm, q[:, qb:], k, rows, 0.125)
+    assert np.array_equal(selg, ref["sel_groups"])
+    assert np.array_equal(sel, ref["sel"])
+    # all keys equal: every score ties, the lowest complete groups and their
+    # lowest chunks win
+    kk = np.ones_like(k)
+    sel, selg, _ = _run(layout, q[:, qb:], kk, L, qb, 0.125, "bf16")
+    assert (selg[:, :, :, :] == np.array([0, 1, 2])).all()
+    assert (sel == np.array([0, 1, 2, 3, 4])).all()
