@@ -42,7 +42,7 @@ class Tensor(ctypes.Structure):
 
 
 EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_columns",
-           "gsa_attn_prefill", "gsa_prefill_tile", "gsa_attn_decode",
+           "gsa_attn_prefill", "gsa_prefill_tile", "gsa_attn_decode", "gsa_attn_decode_noalloc",
            "gsa_decode_workspace_bytes", "gsa_status_str", "gsa_last_error")
 
 _lib = None
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gsa_prefill_tile.argtypes = [I32, I32, P(I32), P(I32)]
     lib.gsa_attn_decode.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32,
                                     V, V, F, V, ctypes.c_size_t, V]
+    lib.gsa_attn_decode_noalloc.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32,
+                                            I32, V, V, F, V]
     lib.gsa_decode_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
     lib.gsa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gsa_status_str.argtypes = [I32]
@@ -258,4 +260,23 @@ def attn_decode(layout: dict, q, k_cache, v_cache, sel=None, sel_groups=None,
                                _bhtd(v_cache), _bhd(o), _ptr(lse), B, Hq, Hkv, d, kv_len,
                                _ptr(sel), _ptr(sel_groups), float(scale), workspace.data_ptr(),
                                workspace.numel(), _stream()))
+    return o, lse
+
+
+def attn_decode_noalloc(layout: dict, q, k_cache, v_cache, sel=None, sel_groups=None,
+                        scale: float | None = None, out_dtype=torch.float32, want_lse: bool = True,
+                        out=None):
+    """``attn_decode`` on the library's fixed per-device scratch (no workspace)."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    Hkv, kv_len = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        o = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    else:
+        o, lse = out
+    _check(lib.gsa_attn_decode_noalloc(ctypes.byref(make_layout(layout)), _bhd(q), _bhtd(k_cache),
+                                       _bhtd(v_cache), _bhd(o), _ptr(lse), B, Hq, Hkv, d, kv_len,
+                                       _ptr(sel), _ptr(sel_groups), float(scale), _stream()))
     return o, lse

@@ -23,6 +23,8 @@
 // separate (max, sum, O) partials, merged in LDS into the split's partial; the
 // last split of a (batch, KV head) to finish (a counter in the workspace)
 // merges all splits with log-sum-exp weights and writes the output.
+#include <mutex>
+
 #include "gsa_internal.h"
 
 namespace gsa {
@@ -420,13 +422,14 @@ extern "C" size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B
   return counters_bytes(B, Hkv) + (size_t)B * Hkv * ns * (Hq / Hkv) * (d + kPartExtra) * sizeof(float);
 }
 
-extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
-                                      gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
-                                      int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
-                                      const int32_t* sel_groups, float scale, void* ws, size_t ws_bytes,
-                                      void* stream) {
-  Lay l;
-  gsa_status st = make_lay(layout, kv_len, 64, &l);
+namespace gsa {
+namespace {
+
+// Argument checks shared by both decode entry points (nothing is launched).
+gsa_status check_decode(const gsa_layout* layout, const gsa_tensor& q, const gsa_tensor& k_cache,
+                        const gsa_tensor& v_cache, const gsa_tensor& o, int B, int Hq, int Hkv, int d,
+                        int kv_len, const int32_t* sel, const int32_t* sel_groups, float scale, Lay* l) {
+  gsa_status st = make_lay(layout, kv_len, 64, l);
   if (st != GSA_OK) return st;
   if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
   if ((st = check_tensor("k_cache", k_cache, d)) != GSA_OK) return st;
@@ -440,19 +443,18 @@ extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gs
   if (d != 64 && d != 128) return fail(GSA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d);
   if (!(scale > 0.f)) return fail(GSA_EINVAL, "scale must be > 0");
   if (kv_len < 1) return fail(GSA_EINVAL, "kv_len %d < 1", kv_len);
-  if (l.k > 64 || l.k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
-  if (l.k > 0 && !sel) return fail(GSA_EINVAL, "sel is required when top_k > 0");
-  if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is required with two levels");
-  if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
-  const size_t need = gsa_decode_workspace_bytes(layout, B, Hq, Hkv, d, kv_len);
-  if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
-  int rps;
-  const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
-  hipStream_t s = (hipStream_t)stream;
+  if (l->k > 64 || l->k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
+  if (l->k > 0 && !sel) return fail(GSA_EINVAL, "sel is required when top_k > 0");
+  if (l->G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is required with two levels");
+  if (l->G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
+  return GSA_OK;
+}
+
+gsa_status launch_decode(const Lay& l, const gsa_tensor& q, const gsa_tensor& k_cache,
+                         const gsa_tensor& v_cache, const gsa_tensor& o, float* lse, int B, int Hq, int Hkv,
+                         int d, int kv_len, const int32_t* sel, const int32_t* sel_groups, float scale,
+                         int* counters, float* part, int ns, int rps, hipStream_t s) {
   const float c2 = scale * kLog2e;
-  int* counters = (int*)ws;
-  float* part = (float*)((char*)ws + counters_bytes(B, Hkv));
 #define GSA_DECODE(D, TO)                                                                             \
   hipLaunchKernelGGL((k_decode<D, TO>), dim3(ns, Hkv, B), dim3(kThreads), 0, s, l,                    \
                      (const unsigned short*)q.ptr, q.stride_b, q.stride_h,                            \
@@ -468,5 +470,95 @@ extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gs
     else GSA_DECODE(64, unsigned short);
   }
 #undef GSA_DECODE
+  return GSA_OK;
+}
+
+// ---- scratch of gsa_attn_decode_noalloc
+// One fixed array per GPU (each device holds its own copy until the process
+// ends): completion counters in a fixed region at the start, which every call
+// leaves at zero, then the split partials of the current call.  Host code
+// never uses the array's name as an address: the device address of the
+// current GPU's copy comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchCounterBytes = 64u << 10;    // up to 16384 (batch, KV head) pairs
+constexpr size_t kScratchBytes = 8u << 20;            // 8 MiB in all
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void k_zero_words(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of this GPU's scratch; on the first call on a device its
+// counter region is cleared by a fill kernel on `s` (no memset node, so the
+// call can sit inside a captured graph).
+gsa_status scratch_ptr(hipStream_t s, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GSA_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(GSA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int n = (int)(kScratchCounterBytes / 4);
+    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, s, (unsigned*)p, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(GSA_EHIP, "clearing the scratch counters: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return GSA_OK;
+}
+
+}  // namespace
+}  // namespace gsa
+
+extern "C" gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
+                                      gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
+                                      int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
+                                      const int32_t* sel_groups, float scale, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  Lay l;
+  gsa_status st = check_decode(layout, q, k_cache, v_cache, o, B, Hq, Hkv, d, kv_len, sel, sel_groups, scale, &l);
+  if (st != GSA_OK) return st;
+  const size_t need = gsa_decode_workspace_bytes(layout, B, Hq, Hkv, d, kv_len);
+  if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
+  int rps;
+  const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
+  int* counters = (int*)ws;
+  float* part = (float*)((char*)ws + counters_bytes(B, Hkv));
+  launch_decode(l, q, k_cache, v_cache, o, lse, B, Hq, Hkv, d, kv_len, sel, sel_groups, scale, counters, part,
+                ns, rps, (hipStream_t)stream);
   return launch_status("gsa_attn_decode");
+}
+
+extern "C" gsa_status gsa_attn_decode_noalloc(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
+                                              gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B,
+                                              int32_t Hq, int32_t Hkv, int32_t d, int32_t kv_len,
+                                              const int32_t* sel, const int32_t* sel_groups, float scale,
+                                              void* stream) {
+  Lay l;
+  gsa_status st = check_decode(layout, q, k_cache, v_cache, o, B, Hq, Hkv, d, kv_len, sel, sel_groups, scale, &l);
+  if (st != GSA_OK) return st;
+  if ((size_t)B * Hkv * sizeof(int) > kScratchCounterBytes)
+    return fail(GSA_EUNSUPPORTED, "batch x KV heads = %lld exceeds the %zu completion counters of the fixed scratch",
+                (long long)B * Hkv, kScratchCounterBytes / sizeof(int));
+  int rps;
+  const int ns = plan_splits(B, Hkv, row_bound(l, kv_len), &rps);
+  const size_t part_bytes = (size_t)B * Hkv * ns * (Hq / Hkv) * (d + kPartExtra) * sizeof(float);
+  if (part_bytes > kScratchBytes - kScratchCounterBytes)
+    return fail(GSA_EUNSUPPORTED, "these sizes need %zu bytes of split partials; the fixed scratch holds %zu",
+                part_bytes, kScratchBytes - kScratchCounterBytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* base = nullptr;
+  if ((st = scratch_ptr(s, &base)) != GSA_OK) return st;
+  launch_decode(l, q, k_cache, v_cache, o, lse, B, Hq, Hkv, d, kv_len, sel, sel_groups, scale, (int*)base,
+                (float*)(base + kScratchCounterBytes), ns, rps, s);
+  return launch_status("gsa_attn_decode_noalloc");
 }

@@ -26,7 +26,8 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates no device memory and keeps no device state between calls.
+ *     allocates no device memory and keeps no device state between calls
+ *     (except gsa_attn_decode_noalloc's fixed scratch array, below).
  *   - Work is only enqueued on `stream` (a hipStream_t; NULL = null stream);
  *     no call synchronises.  Faults inside kernels surface at the caller's
  *     next synchronisation.
@@ -168,16 +169,35 @@ gsa_status gsa_prefill_tile(int32_t dtype, int32_t d, int32_t* block_m, int32_t*
  *   lse      nullable float [B, Hq]
  *   sel      int32 [B, Hkv, 1, top_k]; sel_groups [B, Hkv, 1, l2_top_k] or NULL
  *   ws       device workspace of at least gsa_decode_workspace_bytes(),
- *            256-byte aligned.  Zero-fill it once before its first use: it
- *            starts with per-(batch, KV head) completion counters that every
- *            call leaves at zero again.  Calls that share one workspace must
- *            not overlap (same stream, or serialised by the caller).
+ *            256-byte aligned.  Zero-fill it before its first use: it starts
+ *            with per-(batch, KV head) completion counters that every call
+ *            leaves at zero again (the partials follow them, so zero it again
+ *            before reusing it for a larger batch * KV heads).  Calls that
+ *            share one workspace must not overlap (same stream, or serialised
+ *            by the caller).
  * Requires bf16 inputs, d in {64,128}, Hq/Hkv <= 16. */
 gsa_status gsa_attn_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
                            gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
                            int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
                            const int32_t* sel_groups, float scale, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* gsa_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * gsa_attn_decode; the completion counters and split partials live in a fixed
+ * 8 MiB device array of the library instead (each GPU the library runs on
+ * holds its own copy until the process ends).  Limits: batch * KV heads <=
+ * 16384, and the split partials of the call must fit the array (GSA_EUNSUPPORTED
+ * otherwise, nothing launched).  The first call on a device looks up that
+ * device's copy and clears its counters with a fill kernel on `stream`; every
+ * call leaves them at zero again.  All calls on one GPU share the array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  Allocates nothing. */
+gsa_status gsa_attn_decode_noalloc(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache,
+                                   gsa_tensor v_cache, gsa_tensor o, float* lse, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
+                                   const int32_t* sel_groups, float scale, void* stream);
 
 /* Host only.  Workspace bytes gsa_attn_decode needs for these sizes. */
 size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
