@@ -43,7 +43,8 @@ class Tensor(ctypes.Structure):
 
 EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_columns",
            "gsa_attn_prefill", "gsa_prefill_tile", "gsa_attn_decode", "gsa_attn_decode_noalloc",
-           "gsa_decode_workspace_bytes", "gsa_status_str", "gsa_last_error")
+           "gsa_decode_workspace_bytes", "gsa_decode_step", "gsa_decode_step_workspace_bytes",
+           "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -73,13 +74,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             I32, V, V, F, V]
     lib.gsa_decode_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
     lib.gsa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_decode_step.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32, F,
+                                    V, V, V, ctypes.c_size_t, V]
+    lib.gsa_decode_step_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
+    lib.gsa_decode_step_workspace_bytes.restype = ctypes.c_size_t
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
     lib.gsa_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
         if name not in ("gsa_score_columns", "gsa_decode_workspace_bytes", "gsa_status_str",
-                        "gsa_last_error"):
+                        "gsa_last_error", "gsa_decode_step_workspace_bytes"):
             getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -280,3 +285,35 @@ def attn_decode_noalloc(layout: dict, q, k_cache, v_cache, sel=None, sel_groups=
                                        _bhtd(v_cache), _bhd(o), _ptr(lse), B, Hq, Hkv, d, kv_len,
                                        _ptr(sel), _ptr(sel_groups), float(scale), _stream()))
     return o, lse
+
+
+def decode_step_workspace_bytes(layout: dict, B: int, Hq: int, Hkv: int, d: int, kv_len: int) -> int:
+    return int(load_library().gsa_decode_step_workspace_bytes(ctypes.byref(make_layout(layout)), B, Hq,
+                                                              Hkv, d, kv_len))
+
+
+def decode_step(layout: dict, q, k_cache, v_cache, scale: float | None = None, out_dtype=torch.float32,
+                want_lse: bool = True, workspace=None, out=None):
+    """Fused selection + decode; ``q [B, Hq, d]``, caches ``[B, Hkv, kv_len, d]``.
+
+    Returns (o, lse or None, sel, sel_groups or None).  ``out`` is an optional
+    (o, lse, sel, sel_groups) tuple of preallocated outputs."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    Hkv, kv_len = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = decode_step_workspace_bytes(layout, B, Hq, Hkv, d, kv_len)
+    if workspace is None:   # zero-filled once: the kernels leave their counters at zero
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+        sel = torch.empty((B, Hkv, 1, int(layout.get("top_k", 0))), dtype=torch.int32, device=q.device)
+        selg = (torch.empty((B, Hkv, 1, int(layout["l2_top_k"])), dtype=torch.int32, device=q.device)
+                if is_hierarchical(layout) else None)
+    else:
+        o, lse, sel, selg = out
+    _check(lib.gsa_decode_step(ctypes.byref(make_layout(layout)), _bhd(q), _bhtd(k_cache), _bhtd(v_cache),
+                               _bhd(o), _ptr(lse), B, Hq, Hkv, d, kv_len, float(scale), sel.data_ptr(),
+                               _ptr(selg), workspace.data_ptr(), workspace.numel(), _stream()))
+    return o, lse, sel, selg

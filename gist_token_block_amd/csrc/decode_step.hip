@@ -1,0 +1,781 @@
+// Fused decode step (gsa_decode_step): scoring, per-KV-group top-k (one or two
+// levels) and the split-K attention of one query token per sequence, with
+// every visible K/V row read from HBM once.
+//
+// The method: a query scores the chunks whose gists all precede it against
+// their gist keys only and unfolds the raw tokens of the k best (Simplified
+// Sparse Attention via Gist Tokens, abstract); with gist of gist it first keeps
+// the best groups by their level-2 gists, then the best chunks inside them
+// (Forget, Then Recall ... Gist Sparse Attention, abstract).  It attends to the
+// sinks, every gist (two levels: every level-2 gist and the level-1 gists of
+// the kept groups), its local window and the unfolded raws (UniGist summary,
+// Approach).  A candidate's score for one KV head is the mean over that KV
+// group's query heads (and over the candidate's gists) of q.k * scale.
+//
+// Every scored gist is also a visible row, so scoring costs no extra reads:
+//   phase A (k_step_a, many workgroups per (batch, KV head)): stream the
+//     top-level gist stream (single level: the gists; two levels: the level-2
+//     gists), the sinks and the window; one MFMA product per 16 rows gives the
+//     logits of all query heads, which feed both the attention partial and,
+//     summed over the heads, the candidates' scores.  Each workgroup keeps the
+//     best k of its candidates.  The last workgroup of a (batch, KV head) to
+//     finish merges those lists into the top-level selection; with two levels
+//     it then streams the kept groups' level-1 gists (scoring and attending
+//     them) and picks the chunks.
+//   phase B (k_step_b, many workgroups per (batch, KV head)): stream the raw
+//     rows of the unfolded chunks; the last workgroup merges the partials of
+//     both phases with log-sum-exp weights and writes the output.
+// Rows inside the window are attended only by the window segment, so every
+// row is counted once; top-level gists inside the window are still scored.
+#include <limits.h>
+
+#include "decode_common.h"
+#include "select_net.h"
+
+namespace gsa {
+namespace {
+using namespace dec;
+
+constexpr int kMaxRowsPerSplit = 2048;   // rows one phase-A workgroup scores
+constexpr int kMaxL1Rows = 1024;         // level-1 gist rows of the kept groups
+
+// Row flags of a staged block.
+constexpr int kAttend = 1, kScore = 2;
+
+template <int D> struct StepLds {
+  unsigned short stage0[2 * kRows * D];
+  unsigned short stage1[2 * kRows * D];
+};
+
+// Streams virtual rows [v_begin, v_end) through LDS in 64-row blocks (double
+// buffered, global_load_lds) and folds them into this wave's online-softmax
+// state for all query heads of the group.  rowinfo(v, &pos, &flags) gives the
+// cache position of virtual row v and whether it is attended and/or scored;
+// rows that are scored get the sum over the query heads of their raw logits
+// (q.k) written to rowscore[v - v_begin].
+template <int D, typename RowInfo>
+__device__ void stream_rows(int v_begin, int v_end, RowInfo rowinfo, const unsigned short* __restrict__ kb,
+                            int64_t kst, const unsigned short* __restrict__ vb, int64_t vst,
+                            const bf16x8* qreg, float c2, unsigned short* __restrict__ stage0,
+                            unsigned short* __restrict__ stage1, int (*rowpos)[kRows], int (*rowflag)[kRows],
+                            float* __restrict__ rowscore, f32x4* oacc, float& m_run, float& l_run, float& l_ex) {
+  using C = DCfg<D>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nblk = (v_end - v_begin + kRows - 1) / kRows;
+  if (nblk <= 0) return;
+  const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  auto positions = [&](int blk) {
+    if (tid < kRows) {
+      const int v = v_begin + blk * kRows + tid;
+      int pos, fl = 0;
+      rowinfo(imin(v, v_end - 1), pos, fl);
+      rowpos[blk & 1][tid] = pos;
+      rowflag[blk % 3][tid] = v < v_end ? fl : 0;
+    }
+  };
+  auto fetch = [&](int blk, unsigned short* Kd) {
+    unsigned short* Vd = Kd + kRows * D;
+#pragma unroll
+    for (int it = 0; it < C::NIW; ++it) {
+      const int wi = wave * C::NIW + it;
+      const int row = wi * C::RPI + srow;
+      const int p = rowpos[blk & 1][row];
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)(kb + (int64_t)p * kst + 8 * (sslot ^ dswz_k<D>(row))),
+                                       (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)(vb + (int64_t)p * vst + 8 * (sslot ^ dswz_v<D>(row))),
+                                       (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
+    }
+  };
+  __syncthreads();   // earlier users of rowpos / staging are done
+  positions(0);
+  if (nblk > 1) positions(1);
+  __syncthreads();
+  fetch(0, stage0);
+
+  const int tj = lane & 15;
+  const int trow = 4 * grp + (tj >> 2);
+  int k_off[C::KS], tr_off[C::MT];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int row = 16 * wave + col, pc = grp + 4 * ks;
+    k_off[ks] = row * D + 8 * (pc ^ dswz_k<D>(row));
+    asm volatile("" : "+v"(k_off[ks]));
+  }
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) {
+    const int row = 16 * wave + trow, pc = 2 * mt + ((tj & 3) >> 1);
+    tr_off[mt] = row * D + 8 * (pc ^ dswz_v<D>(row)) + 4 * (tj & 1);
+    asm volatile("" : "+v"(tr_off[mt]));
+  }
+
+  auto step = [&](int blk, const unsigned short* Kb, unsigned short* next) {
+    // One barrier per block: this wave's copies of blk have landed, every
+    // wave is done with blk - 1 (whose staging buffer the next fetch reuses
+    // and whose row-flag slot positions(blk + 2) rewrites: flags rotate over
+    // three slots, positions over two), and the row table of blk + 1 is set.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int fl[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) fl[e] = rowflag[blk % 3][16 * wave + 4 * grp + e];
+    if (blk + 1 < nblk) fetch(blk + 1, next);
+    if (blk + 2 < nblk) positions(blk + 2);
+    const unsigned short* Vb = Kb + kRows * D;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + k_off[ks]);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], s, 0, 0, 0);
+    }
+    // s[e]: key row 16 wave + 4 grp + e of the block, head slot col (zero for
+    // slots past the group's heads, whose q rows are zero)
+    if (rowscore) {
+      bool any = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) any |= (fl[e] & kScore) != 0;
+      if (__ballot(any)) {
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = s[e];
+#pragma unroll
+          for (int j = 1; j < 16; j <<= 1) v += xor_lane(v, j);
+          t[e] = v;
+        }
+        if (col == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = blk * kRows + 16 * wave + 4 * grp + e;
+            if (fl[e] & kScore) rowscore[r] = t[e];
+          }
+        }
+      }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!(fl[e] & kAttend)) s[e] = -__builtin_inff();
+      mx = fmaxf(mx, s[e]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = fmaxf(m_run, mx * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, -m_new));
+    const unsigned w0 = pack_bf16x2(s[0], s[1]), w1 = pack_bf16x2(s[2], s[3]);
+    const bf16x2 ones = bf16x2{(__bf16)1.0f, (__bf16)1.0f};
+    float ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.f, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, ps, false);
+    float pe = (s[0] + s[1]) + (s[2] + s[3]);
+    ps += __shfl_xor(ps, 16);
+    pe += __shfl_xor(pe, 16);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+      ps = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const auto se = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(pe), false, false);
+      pe = __uint_as_float(se[0]) + __uint_as_float(se[1]);
+    }
+    l_run = l_run * alpha + ps;
+    l_ex = l_ex * alpha + pe;
+    m_run = m_new;
+    const bf16x4 pb = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      oacc[mt] *= alpha;
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(Vb + tr_off[mt]));
+      oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, pb), oacc[mt], 0, 0, 0);
+    }
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(blk, stage0, stage1);
+    if (blk + 1 < nblk) step(blk + 1, stage1, stage0);
+  }
+  __syncthreads();   // staging buffers and row tables are reused by the caller
+}
+
+// Merges the 4 waves' online-softmax states into one partial per query head
+// and stores it at dst ([G][D + kPartExtra]) with device-scope stores.  The
+// staging memory `scratch` (>= 4 * 16 * D floats) is clobbered.
+template <int D>
+__device__ void store_partial(const f32x4* oacc, float m_run, float l_run, float l_ex, int G, float* wstat,
+                              float* scratch, float* __restrict__ dst) {
+  using C = DCfg<D>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  constexpr int PS = D + kPartExtra;
+  float* cm = wstat;
+  float* cl = wstat + 64;
+  float* ce = wstat + 128;
+  if (grp == 0) {
+    cm[wave * 16 + col] = m_run;
+    cl[wave * 16 + col] = l_run;
+    ce[wave * 16 + col] = l_ex;
+  }
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) scratch[(wave * 16 + col) * D + 16 * mt + 4 * grp + e] = oacc[mt][e];
+  __syncthreads();
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int hd = x / D, dd = x - hd * D;
+    float M = kNegBig;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, cm[w * 16 + hd]);
+    float L = 0.f, LE = 0.f, O = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(cm[w * 16 + hd] - M);
+      L += cl[w * 16 + hd] * f;
+      LE += ce[w * 16 + hd] * f;
+      O += scratch[(w * 16 + hd) * D + dd] * f;
+    }
+    st_dev(&dst[hd * PS + dd], O);
+    if (dd == 0) {
+      st_dev(&dst[hd * PS + D], M);
+      st_dev(&dst[hd * PS + D + 1], L);
+      st_dev(&dst[hd * PS + D + 2], LE);
+    }
+  }
+  __syncthreads();
+}
+
+// Best-first top list of candidates [0, ncand) scored by score(e) with ids
+// id(e), merged across the 4 waves; wave 0's lanes hold the result (rs, ri).
+template <typename ScoreFn, typename IdFn>
+__device__ void rank_candidates(int ncand, ScoreFn score, IdFn id, float* lds_s, int* lds_i, float& rs, int& ri) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  rs = -__builtin_inff();
+  ri = INT_MAX;
+  bool empty = true;
+  for (int b0 = wave * 64; b0 < ncand; b0 += 4 * 64) {
+    const int e = b0 + lane;
+    float s = -__builtin_inff();
+    int d = INT_MAX;
+    if (e < ncand) {
+      s = nan_to_neg_inf(score(e));
+      d = id(e);
+    }
+    wave_sort_best_first(s, d);
+    if (empty) {
+      rs = s;
+      ri = d;
+      empty = false;
+    } else {
+      wave_merge(rs, ri, s, d);
+    }
+  }
+  __syncthreads();
+  lds_s[wave * 64 + lane] = rs;
+  lds_i[wave * 64 + lane] = ri;
+  __syncthreads();
+  for (int st = 1; st < 4; st <<= 1) {
+    if ((wave & (2 * st - 1)) == 0 && wave + st < 4) {
+      wave_merge(rs, ri, lds_s[(wave + st) * 64 + lane], lds_i[(wave + st) * 64 + lane]);
+      lds_s[wave * 64 + lane] = rs;
+      lds_i[wave * 64 + lane] = ri;
+    }
+    __syncthreads();
+  }
+}
+
+struct StepArgs {
+  Lay l;
+  const unsigned short* q;
+  int64_t qsb, qsh;
+  const unsigned short* kc;
+  int64_t ksb, kst, ksh;
+  const unsigned short* vc;
+  int64_t vsb, vst, vsh;
+  int Hq, Hkv, kv_len;
+  float c2, score_mul1, score_mul2;   // logit scale (log2 units); score scales for levels 1 and 2
+  int* counters;                      // [2][B*Hkv]: phase A, phase B
+  float* list_s;                      // [B*Hkv][nsa][64]
+  int* list_i;
+  float* part;                        // [B*Hkv][nslot][G][D + kPartExtra]
+  int nsa, rpa, nsb, rpb, nslot;
+  int* sel;                           // [B*Hkv][k]      (out)
+  int* selg;                          // [B*Hkv][k2]     (out, two levels)
+  void* o;
+  int64_t osb, osh;
+  float* lse;
+};
+
+template <int D>
+__device__ void load_q(const StepArgs& a, int b, int h, bf16x8* qreg) {
+  using C = DCfg<D>;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int G = a.Hq / a.Hkv;
+  const unsigned short* qrow = a.q + b * a.qsb + (int64_t)(h * G + imin(col, G - 1)) * a.qsh;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 8 * grp + 32 * ks);
+    if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
+    qreg[ks] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// ---------------------------------------------------------------- phase A
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_step_a(StepArgs a) {
+  using C = DCfg<D>;
+  const Lay& l = a.l;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.Hq / a.Hkv;
+  const int i = a.kv_len - 1;
+  const int lo = imax(0, i - l.W1 + 1);
+  const size_t gidx = (size_t)b * a.Hkv + h;
+  const bool two = l.G2 > 0;
+  const int top = two ? K_GIST2 : K_GIST;            // the stream scored here
+  const int per = two ? l.g2 : l.g;                  // its gists per candidate
+  const int ktop = two ? l.k2 : l.k;                 // candidates kept
+  const int ncand = count_below(l, top, i) / per;    // complete candidates
+  const int natt = count_below(l, top, lo);          // top gists before the window
+  const int nsc = ncand * per;                       // top gists that are scored
+  const int ntop = imax(natt, nsc);
+  const int nsink = imin(l.S, lo);
+  const int total = ntop + nsink + (i - lo + 1);     // [top | sinks | window]
+
+  __shared__ __attribute__((aligned(1024))) StepLds<D> lds;
+  __shared__ int rowpos[2][kRows], rowflag[3][kRows];
+  __shared__ float rowscore[kMaxRowsPerSplit];
+  __shared__ float lds_s[4 * 64];
+  __shared__ int lds_i[4 * 64];
+  __shared__ float wstat[192];
+  __shared__ int kept[64];
+  __shared__ int am_last;
+
+  bf16x8 qreg[C::KS];
+  load_q<D>(a, b, h, qreg);
+  const unsigned short* kb = a.kc + b * a.ksb + h * a.ksh;
+  const unsigned short* vb = a.vc + b * a.vsb + h * a.vsh;
+  const int v_begin = imin(split * a.rpa, total);
+  const int v_end = imin(v_begin + a.rpa, total);
+  auto info = [&](int v, int& pos, int& fl) {
+    if (v < ntop) {
+      pos = pos_of(l, top, v);
+      fl = (v < natt ? kAttend : 0) | (v < nsc ? kScore : 0);
+    } else if (v < ntop + nsink) {
+      pos = v - ntop;
+      fl = kAttend;
+    } else {
+      pos = lo + (v - ntop - nsink);
+      fl = kAttend;
+    }
+  };
+  f32x4 oacc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f, l_ex = 0.f;
+  stream_rows<D>(v_begin, v_end, info, kb, a.kst, vb, a.vst, qreg, a.c2, lds.stage0, lds.stage1, rowpos, rowflag,
+                 ktop > 0 ? rowscore : nullptr, oacc, m_run, l_run, l_ex);
+  float* gpart = a.part + gidx * a.nslot * G * (D + kPartExtra);
+  store_partial<D>(oacc, m_run, l_run, l_ex, G, wstat, reinterpret_cast<float*>(lds.stage0),
+                   gpart + (size_t)split * G * (D + kPartExtra));
+
+  // this split's best candidates (those whose gists it scored; splits start
+  // at multiples of `per`, so no candidate straddles two)
+  float* gls = a.list_s + gidx * a.nsa * 64;
+  int* gli = a.list_i + gidx * a.nsa * 64;
+  if (ktop > 0) {
+    const int c0 = v_begin / per;
+    const int c1 = imax(c0, imin(v_end, nsc) / per);
+    float rs;
+    int ri;
+    rank_candidates(
+        c1 - c0,
+        [&](int e) {
+          float s = 0.f;
+          for (int t = 0; t < per; ++t) s += rowscore[(c0 + e) * per + t - v_begin];
+          return s * a.score_mul2;
+        },
+        [&](int e) { return c0 + e; }, lds_s, lds_i, rs, ri);
+    if (wave == 0) {
+      st_dev(&gls[split * 64 + lane], rs);
+      __hip_atomic_store(&gli[split * 64 + lane], ri, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // the last split of this (batch, KV head) makes the selection
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&a.counters[gidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    am_last = prev == a.nsa - 1;
+  }
+  __syncthreads();
+  if (!am_last) return;
+  int nkept = 0;
+  if (ktop > 0) {
+    // merge the splits' lists: wave w takes lists w, w + 4, ... then the tree
+    float rs = -__builtin_inff();
+    int ri = INT_MAX;
+    for (int sp = wave; sp < a.nsa; sp += 4) {
+      const float xs = ld_dev(&gls[sp * 64 + lane]);
+      const int xi = __hip_atomic_load(&gli[sp * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sp == wave) {
+        rs = xs;
+        ri = xi;
+      } else {
+        wave_merge(rs, ri, xs, xi);
+      }
+    }
+    lds_s[wave * 64 + lane] = rs;
+    lds_i[wave * 64 + lane] = ri;
+    __syncthreads();
+    for (int st = 1; st < 4; st <<= 1) {
+      if ((wave & (2 * st - 1)) == 0 && wave + st < 4) {
+        wave_merge(rs, ri, lds_s[(wave + st) * 64 + lane], lds_i[(wave + st) * 64 + lane]);
+        lds_s[wave * 64 + lane] = rs;
+        lds_i[wave * 64 + lane] = ri;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      const int nv = place_ascending(lane < ktop ? ri : INT_MAX, ktop, (two ? a.selg + gidx * l.k2 : a.sel + gidx * l.k),
+                                     kept);
+      if (lane == 0) lds_i[0] = nv;
+    }
+    __syncthreads();
+    nkept = lds_i[0];
+  }
+  float* extra = gpart + (size_t)a.nsa * G * (D + kPartExtra);
+  if (!two) {
+    if (tid == 0) __hip_atomic_store(&a.counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // no level-1 stage: an empty partial in the extra slot
+    for (int x = tid; x < G * (D + kPartExtra); x += kThreads) {
+      const int dd = x % (D + kPartExtra);
+      st_dev(&extra[x], dd == D ? kNegBig : 0.f);
+    }
+    return;
+  }
+
+  // two levels: the level-1 gists of the kept groups, scored and (before the
+  // window) attended; candidates are every chunk of a kept group (complete,
+  // as the group is)
+  const int ngr = ncand;
+  const int cpg = l.G2;                    // chunks per group
+  const int rows_pg = cpg * l.g;           // level-1 gists per group
+  const int nl1 = imin(nkept * rows_pg, kMaxL1Rows);
+  const int nl1_att = count_below(l, K_GIST, lo);   // level-1 gists before the window
+  auto info1 = [&](int v, int& pos, int& fl) {
+    const int e = v / rows_pg, t = v - e * rows_pg;
+    const int gr = iclamp(kept[e], 0, imax(ngr - 1, 0));
+    const int u = gr * rows_pg + t;
+    pos = pos_of(l, K_GIST, u);
+    fl = kScore | (u < nl1_att ? kAttend : 0);
+  };
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  m_run = kNegBig;
+  l_run = 0.f;
+  l_ex = 0.f;
+  stream_rows<D>(0, nl1, info1, kb, a.kst, vb, a.vst, qreg, a.c2, lds.stage0, lds.stage1, rowpos, rowflag, rowscore,
+                 oacc, m_run, l_run, l_ex);
+  store_partial<D>(oacc, m_run, l_run, l_ex, G, wstat, reinterpret_cast<float*>(lds.stage0), extra);
+  float rs;
+  int ri;
+  rank_candidates(
+      nl1 / l.g,
+      [&](int e) {
+        float s = 0.f;
+        for (int t = 0; t < l.g; ++t) s += rowscore[e * l.g + t];
+        return s * a.score_mul1;
+      },
+      [&](int e) {
+        const int gi = e / cpg;
+        return iclamp(kept[gi], 0, imax(ngr - 1, 0)) * cpg + (e - gi * cpg);
+      },
+      lds_s, lds_i, rs, ri);
+  if (wave == 0) place_ascending(lane < l.k ? ri : INT_MAX, l.k, a.sel + gidx * l.k, nullptr);
+  if (tid == 0) __hip_atomic_store(&a.counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- phase B
+template <int D, typename TO>
+__global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
+  using C = DCfg<D>;
+  const Lay& l = a.l;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.Hq / a.Hkv;
+  const int i = a.kv_len - 1;
+  const int lo = imax(0, i - l.W1 + 1);
+  const size_t gidx = (size_t)b * a.Hkv + h;
+
+  __shared__ __attribute__((aligned(1024))) StepLds<D> lds;
+  __shared__ int rowpos[2][kRows], rowflag[3][kRows];
+  __shared__ float wstat[192];
+  __shared__ int seg_start[65], seg_base[64];
+  __shared__ int nseg, am_last;
+
+  // unfolded chunks' raws before the window: one contiguous run per chunk,
+  // laid out by an exclusive scan over the selection (lanes of wave 0)
+  if (wave == 0) {
+    const int nch = count_below(l, K_GIST, i) / l.g;   // complete chunks
+    int len = 0, st = 0;
+    if (lane < l.k) {
+      const int m = a.sel[gidx * l.k + lane];
+      if (m >= 0 && m < nch) {
+        st = pos_of(l, K_RAW, m * l.c);
+        len = iclamp(lo - st, 0, l.c);
+      }
+    }
+    int incl = len;
+#pragma unroll
+    for (int j = 1; j < 64; j <<= 1) {
+      const int t = __shfl_up(incl, j);
+      if (lane >= j) incl += t;
+    }
+    if (lane < 64) {
+      seg_start[lane] = incl - len;
+      seg_base[lane] = st;
+    }
+    if (lane == 63) {
+      seg_start[64] = incl;
+      nseg = 64;
+    }
+  }
+  __syncthreads();
+  const int total = seg_start[64];
+  auto info = [&](int v, int& pos, int& fl) {
+    int lo_s = 0, hi_s = 63;    // last run with start <= v (empty runs are skipped by the search)
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (seg_start[mid] <= v) lo_s = mid;
+      else hi_s = mid - 1;
+    }
+    pos = seg_base[lo_s] + (v - seg_start[lo_s]);
+    fl = kAttend;
+  };
+  bf16x8 qreg[C::KS];
+  load_q<D>(a, b, h, qreg);
+  const unsigned short* kb = a.kc + b * a.ksb + h * a.ksh;
+  const unsigned short* vb = a.vc + b * a.vsb + h * a.vsh;
+  const int v_begin = imin(split * a.rpb, total);
+  const int v_end = imin(v_begin + a.rpb, total);
+  f32x4 oacc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f, l_ex = 0.f;
+  stream_rows<D>(v_begin, v_end, info, kb, a.kst, vb, a.vst, qreg, a.c2, lds.stage0, lds.stage1, rowpos, rowflag,
+                 nullptr, oacc, m_run, l_run, l_ex);
+  constexpr int PS = D + kPartExtra;
+  float* gpart = a.part + gidx * a.nslot * G * PS;
+  store_partial<D>(oacc, m_run, l_run, l_ex, G, wstat, reinterpret_cast<float*>(lds.stage0),
+                   gpart + (size_t)(a.nsa + 1 + split) * G * PS);
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int* cnt = a.counters + (size_t)gridDim.z * a.Hkv;   // phase-B counters
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(&cnt[gidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    am_last = prev == a.nsb - 1;
+  }
+  __syncthreads();
+  if (!am_last) return;
+  // merge every slot (phase A splits, the level-1 slot, phase B splits)
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int hd = x / D, dd = x - hd * D;
+    float Mr = kNegBig, Lr = 0.f, LEr = 0.f, Or = 0.f;
+    for (int sp0 = 0; sp0 < a.nslot; sp0 += 16) {
+      float po[16], pm[16], pl[16], pe[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float* pp = gpart + (imin(sp0 + j, a.nslot - 1) * G + hd) * PS;
+        po[j] = ld_dev(&pp[dd]);
+        pm[j] = ld_dev(&pp[D]);
+        pl[j] = ld_dev(&pp[D + 1]);
+        pe[j] = a.lse && dd == 0 ? ld_dev(&pp[D + 2]) : 0.f;
+      }
+      float mb = Mr;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sp0 + j < a.nslot) mb = fmaxf(mb, pm[j]);
+      const float al = __builtin_amdgcn_exp2f(Mr - mb);
+      Lr *= al;
+      LEr *= al;
+      Or *= al;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (sp0 + j < a.nslot) {
+          const float wgt = __builtin_amdgcn_exp2f(pm[j] - mb);
+          Lr = fmaf(pl[j], wgt, Lr);
+          LEr = fmaf(pe[j], wgt, LEr);
+          Or = fmaf(po[j], wgt, Or);
+        }
+      }
+      Mr = mb;
+    }
+    const float val = Or / Lr;
+    TO* orow = reinterpret_cast<TO*>(a.o) + b * a.osb + (int64_t)(h * G + hd) * a.osh;
+    if constexpr (sizeof(TO) == 4) {
+      orow[dd] = val;
+    } else {
+      orow[dd] = (TO)(pack_bf16x2(val, 0.f) & 0xffffu);
+    }
+    if (a.lse && dd == 0) a.lse[(size_t)b * a.Hq + h * G + hd] = (Mr + __log2f(LEr)) * kLn2;
+  }
+  if (tid == 0) __hip_atomic_store(&cnt[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- planning
+struct StepPlan {
+  int nsa, rpa, nsb, rpb, nslot;
+  size_t off_lists_s, off_lists_i, off_part, bytes;
+};
+
+int device_cus() {
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return cus;
+}
+
+gsa_status plan_step(const Lay& l, int B, int Hq, int Hkv, int d, int kv_len, StepPlan* p) {
+  const bool two = l.G2 > 0;
+  const int i = kv_len - 1;
+  const int lo = imax(0, i - l.W1 + 1);
+  const int top = two ? K_GIST2 : K_GIST;
+  const int per = two ? l.g2 : l.g;
+  const int ncand = count_below(l, top, i) / per;
+  const int rows_a = imax(count_below(l, top, lo), ncand * per) + imin(l.S, lo) + (i - lo + 1);
+  const int groups = imax(1, B * Hkv);
+  const int target = 2 * device_cus();   // workgroups per phase: about two per CU
+  // phase A: rows per split a multiple of 64 and of `per`, at most kMaxRowsPerSplit
+  int ns = iclamp((target + groups - 1) / groups, 1, kMaxSplit);
+  ns = imin(ns, imax(1, (rows_a + kRows - 1) / kRows));
+  int unit = kRows;
+  while (unit % per) unit += kRows;
+  int rp = ((rows_a + ns - 1) / ns + unit - 1) / unit * unit;
+  if (rp > kMaxRowsPerSplit) {
+    rp = kMaxRowsPerSplit / unit * unit;
+    if (rp < unit) return fail(GSA_EUNSUPPORTED, "gists per candidate %d too large", per);
+  }
+  p->rpa = rp;
+  p->nsa = imax(1, (rows_a + rp - 1) / rp);
+  if (p->nsa > kMaxSplit)
+    return fail(GSA_EUNSUPPORTED, "%d rows per (batch, KV head) need more than %d splits", rows_a, kMaxSplit);
+  // phase B: at most k * c raw rows
+  const int rows_b = l.k * l.c;
+  int nb = iclamp((target + groups - 1) / groups, 1, kMaxSplit);
+  nb = imin(nb, imax(1, (rows_b + kRows - 1) / kRows));
+  p->rpb = imax(kRows, ((rows_b + nb - 1) / nb + kRows - 1) / kRows * kRows);
+  p->nsb = imax(1, (rows_b + p->rpb - 1) / p->rpb);
+  p->nslot = p->nsa + 1 + p->nsb;
+  const size_t cb = ((size_t)2 * groups * sizeof(int) + 255) / 256 * 256;
+  const size_t lists = (size_t)groups * p->nsa * 64;
+  p->off_lists_s = cb;
+  p->off_lists_i = cb + lists * sizeof(float);
+  p->off_part = p->off_lists_i + (lists * sizeof(int) + 255) / 256 * 256;
+  p->bytes = p->off_part + (size_t)groups * p->nslot * (Hq / Hkv) * (d + kPartExtra) * sizeof(float);
+  return GSA_OK;
+}
+
+gsa_status check_step(const gsa_layout* layout, const gsa_tensor& q, const gsa_tensor& k_cache,
+                      const gsa_tensor& v_cache, const gsa_tensor& o, int B, int Hq, int Hkv, int d, int kv_len,
+                      float scale, Lay* l) {
+  gsa_status st = make_lay(layout, kv_len, 64, l);
+  if (st != GSA_OK) return st;
+  if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
+  if ((st = check_tensor("k_cache", k_cache, d)) != GSA_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, d)) != GSA_OK) return st;
+  if ((st = check_tensor("o", o, d)) != GSA_OK) return st;
+  if (q.dtype != GSA_BF16 || k_cache.dtype != GSA_BF16 || v_cache.dtype != GSA_BF16)
+    return fail(GSA_EUNSUPPORTED, "the decode step takes bf16 q and caches");
+  if (o.dtype != GSA_F32 && o.dtype != GSA_BF16) return fail(GSA_EINVAL, "o dtype");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(GSA_EINVAL, "bad head counts B=%d Hq=%d Hkv=%d", B, Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(GSA_EUNSUPPORTED, "more than 16 query heads per KV head");
+  if (d != 64 && d != 128) return fail(GSA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!(scale > 0.f)) return fail(GSA_EINVAL, "scale must be > 0");
+  if (kv_len < 1) return fail(GSA_EINVAL, "kv_len %d < 1", kv_len);
+  if (l->k < 1 || l->k > 64) return fail(GSA_EUNSUPPORTED, "top_k %d outside [1, 64]", l->k);
+  if (l->G2 > 0 && l->k2 > 64) return fail(GSA_EUNSUPPORTED, "l2_top_k %d > 64", l->k2);
+  if (l->G2 > 0 && (long long)l->k2 * l->G2 * l->g > kMaxL1Rows)
+    return fail(GSA_EUNSUPPORTED, "l2_top_k * l2_chunks * gists_per_chunk = %lld level-1 rows (at most %d)",
+                (long long)l->k2 * l->G2 * l->g, kMaxL1Rows);
+  if (l->G2 > 0 && (long long)l->k2 * l->G2 > 64 * 64)
+    return fail(GSA_EUNSUPPORTED, "too many level-1 candidates");
+  return GSA_OK;
+}
+
+}  // namespace
+}  // namespace gsa
+
+using namespace gsa;
+
+extern "C" size_t gsa_decode_step_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
+                                                  int32_t d, int32_t kv_len) {
+  Lay l;
+  if (make_lay(layout, kv_len, 64, &l) != GSA_OK || kv_len < 1 || B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv) return 0;
+  StepPlan p;
+  if (plan_step(l, B, Hq, Hkv, d, kv_len, &p) != GSA_OK) return 0;
+  return p.bytes;
+}
+
+extern "C" gsa_status gsa_decode_step(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache, gsa_tensor v_cache,
+                                      gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                      int32_t kv_len, float scale, int32_t* sel, int32_t* sel_groups, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  Lay l;
+  gsa_status st = check_step(layout, q, k_cache, v_cache, o, B, Hq, Hkv, d, kv_len, scale, &l);
+  if (st != GSA_OK) return st;
+  if (!sel) return fail(GSA_EINVAL, "sel is NULL");
+  if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is NULL with two levels");
+  if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
+  StepPlan p;
+  if ((st = plan_step(l, B, Hq, Hkv, d, kv_len, &p)) != GSA_OK) return st;
+  if (!ws || ws_bytes < p.bytes) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", p.bytes, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
+  char* w = (char*)ws;
+  StepArgs a;
+  a.l = l;
+  a.q = (const unsigned short*)q.ptr;
+  a.qsb = q.stride_b;
+  a.qsh = q.stride_h;
+  a.kc = (const unsigned short*)k_cache.ptr;
+  a.ksb = k_cache.stride_b;
+  a.kst = k_cache.stride_t;
+  a.ksh = k_cache.stride_h;
+  a.vc = (const unsigned short*)v_cache.ptr;
+  a.vsb = v_cache.stride_b;
+  a.vst = v_cache.stride_t;
+  a.vsh = v_cache.stride_h;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.kv_len = kv_len;
+  a.c2 = scale * kLog2e;
+  const int G = Hq / Hkv;
+  a.score_mul1 = scale / (float)(G * l.g);
+  a.score_mul2 = l.G2 > 0 ? scale / (float)(G * l.g2) : a.score_mul1;
+  a.counters = (int*)w;
+  a.list_s = (float*)(w + p.off_lists_s);
+  a.list_i = (int*)(w + p.off_lists_i);
+  a.part = (float*)(w + p.off_part);
+  a.nsa = p.nsa;
+  a.rpa = p.rpa;
+  a.nsb = p.nsb;
+  a.rpb = p.rpb;
+  a.nslot = p.nslot;
+  a.sel = sel;
+  a.selg = sel_groups;
+  a.o = o.ptr;
+  a.osb = o.stride_b;
+  a.osh = o.stride_h;
+  a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128) {
+    hipLaunchKernelGGL((k_step_a<128>), dim3(p.nsa, Hkv, B), dim3(kThreads), 0, s, a);
+    if (o.dtype == GSA_F32) hipLaunchKernelGGL((k_step_b<128, float>), dim3(p.nsb, Hkv, B), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_step_b<128, unsigned short>), dim3(p.nsb, Hkv, B), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_step_a<64>), dim3(p.nsa, Hkv, B), dim3(kThreads), 0, s, a);
+    if (o.dtype == GSA_F32) hipLaunchKernelGGL((k_step_b<64, float>), dim3(p.nsb, Hkv, B), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_step_b<64, unsigned short>), dim3(p.nsb, Hkv, B), dim3(kThreads), 0, s, a);
+  }
+  return launch_status("gsa_decode_step");
+}

@@ -199,6 +199,35 @@ gsa_status gsa_attn_decode_noalloc(const gsa_layout* layout, gsa_tensor q, gsa_t
                                    int32_t Hkv, int32_t d, int32_t kv_len, const int32_t* sel,
                                    const int32_t* sel_groups, float scale, void* stream);
 
+/* Fused decode step: gsa_score_select followed by gsa_attn_decode for one
+ * query per sequence at position kv_len - 1 (selective unfolding: SSA
+ * abstract; gist of gist: GSA abstract; sink + gist + window: UniGist summary,
+ * Approach), in two kernels that read every visible K/V row from HBM once: the
+ * scored gists are visible rows, so their logits give both the scores and the
+ * attention.  Results are those of the two separate calls up to fp32 rounding
+ * of the scores (a selection can differ only where two candidates' scores
+ * are within rounding of each other).
+ *   q, o, k_cache, v_cache, lse   as for gsa_attn_decode
+ *   sel         int32 [B, Hkv, 1, top_k] (out): the unfolded chunks, ascending,
+ *               -1 padded
+ *   sel_groups  two levels: int32 [B, Hkv, 1, l2_top_k] (out); else NULL
+ *   ws          device workspace of at least gsa_decode_step_workspace_bytes(),
+ *               256-byte aligned, zero-filled before its first use (it starts
+ *               with per-(batch, KV head) counters that every call leaves at
+ *               zero; zero it again before reusing it for a larger
+ *               batch * KV heads).  Calls sharing a workspace must not overlap.
+ * Requires bf16 inputs, d in {64, 128}, Hq/Hkv <= 16, 1 <= top_k <= 64,
+ * l2_top_k <= 64 and l2_top_k * l2_chunks * gists_per_chunk <= 1024. */
+gsa_status gsa_decode_step(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache, gsa_tensor v_cache,
+                           gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                           int32_t kv_len, float scale, int32_t* sel, int32_t* sel_groups, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Host only.  Workspace bytes gsa_decode_step needs for these sizes (0 if the
+ * sizes are invalid). */
+size_t gsa_decode_step_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t d, int32_t kv_len);
+
 /* Host only.  Workspace bytes gsa_attn_decode needs for these sizes. */
 size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t d, int32_t kv_len);
