@@ -44,7 +44,8 @@ class Tensor(ctypes.Structure):
 EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_columns",
            "gsa_attn_prefill", "gsa_prefill_tile", "gsa_attn_decode", "gsa_attn_decode_noalloc",
            "gsa_decode_workspace_bytes", "gsa_decode_step", "gsa_decode_step_workspace_bytes",
-           "gsa_status_str", "gsa_last_error")
+           "gsa_compact_slots", "gsa_compact_gists", "gsa_compact_append", "gsa_compact_decode",
+           "gsa_compact_decode_workspace_bytes", "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -78,13 +79,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     V, V, V, ctypes.c_size_t, V]
     lib.gsa_decode_step_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
     lib.gsa_decode_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_compact_slots.argtypes = [LP, I32]
+    lib.gsa_compact_slots.restype = I32
+    lib.gsa_compact_gists.argtypes = [LP, I32]
+    lib.gsa_compact_gists.restype = I32
+    lib.gsa_compact_append.argtypes = [LP, Tensor, Tensor, I32, I32, I32, I32, I32, Tensor, Tensor, I32, V]
+    lib.gsa_compact_decode.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32, I32, F,
+                                       V, ctypes.c_size_t, V]
+    lib.gsa_compact_decode_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
+    lib.gsa_compact_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
     lib.gsa_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
         if name not in ("gsa_score_columns", "gsa_decode_workspace_bytes", "gsa_status_str",
-                        "gsa_last_error", "gsa_decode_step_workspace_bytes"):
+                        "gsa_last_error", "gsa_decode_step_workspace_bytes", "gsa_compact_slots",
+                        "gsa_compact_gists", "gsa_compact_decode_workspace_bytes"):
             getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -317,3 +328,47 @@ def decode_step(layout: dict, q, k_cache, v_cache, scale: float | None = None, o
                                _bhd(o), _ptr(lse), B, Hq, Hkv, d, kv_len, float(scale), sel.data_ptr(),
                                _ptr(selg), workspace.data_ptr(), workspace.numel(), _stream()))
     return o, lse, sel, selg
+
+
+def compact_slots(layout: dict, gist_capacity: int) -> int:
+    return int(load_library().gsa_compact_slots(ctypes.byref(make_layout(layout)), gist_capacity))
+
+
+def compact_gists(layout: dict, seq_len: int) -> int:
+    return int(load_library().gsa_compact_gists(ctypes.byref(make_layout(layout)), seq_len))
+
+
+def compact_append(layout: dict, k_new, v_new, pos0: int, k_cache, v_cache, gist_capacity: int):
+    """Append tokens ``k_new``/``v_new [B, n, Hkv, d]`` at positions
+    ``[pos0, pos0 + n)`` to compact caches ``[B, Hkv, slots, d]``."""
+    lib = load_library()
+    B, n, Hkv, d = k_new.shape
+    _check(lib.gsa_compact_append(ctypes.byref(make_layout(layout)), _bthd(k_new), _bthd(v_new), B, Hkv, d,
+                                  pos0, n, _bhtd(k_cache), _bhtd(v_cache), gist_capacity, _stream()))
+
+
+def compact_decode(layout: dict, q, k_cache, v_cache, pos: int, gist_capacity: int,
+                   scale: float | None = None, out_dtype=torch.float32, want_lse: bool = True,
+                   workspace=None, out=None):
+    """Decode ``q [B, Hq, d]`` at position ``pos`` over compact caches."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if workspace is None:
+        need = int(lib.gsa_compact_decode_workspace_bytes(ctypes.byref(make_layout(layout)), B, Hq, Hkv, d, pos))
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    else:
+        o, lse = out
+    _check(lib.gsa_compact_decode(ctypes.byref(make_layout(layout)), _bhd(q), _bhtd(k_cache), _bhtd(v_cache),
+                                  _bhd(o), _ptr(lse), B, Hq, Hkv, d, pos, gist_capacity, float(scale),
+                                  workspace.data_ptr(), workspace.numel(), _stream()))
+    return o, lse
+
+
+def compact_decode_workspace_bytes(layout: dict, B: int, Hq: int, Hkv: int, d: int, pos: int) -> int:
+    return int(load_library().gsa_compact_decode_workspace_bytes(ctypes.byref(make_layout(layout)), B, Hq, Hkv,
+                                                                 d, pos))

@@ -228,6 +228,49 @@ gsa_status gsa_decode_step(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_
 size_t gsa_decode_step_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
                                        int32_t d, int32_t kv_len);
 
+/* ---- Compact cache: fixed-layout decode with real KV removal.
+ * With the fixed layout (top_k = 0, one level) a query sees only the sinks,
+ * every gist and its window (UniGist summary, Approach), so raw tokens that
+ * have left the window can be removed from the cache (UniGist summary:
+ * removal of the compressed tokens at inference; the Study page, §2
+ * Preliminaries: 75% of the KV memory saved at ratio 4).  A compact cache of
+ * one (batch, KV head) has gsa_compact_slots() rows:
+ *   [ n_sink sink slots | gist_capacity gist slots | W ring slots ]
+ * (W = max(window, 1)); the t-th gist of the sequence lives in gist slot t, a
+ * raw token at position p in ring slot p mod W.  Caches are [B, Hkv, slots, d]
+ * bf16 by strides; other layouts return GSA_EUNSUPPORTED. */
+
+/* Host only.  Rows of a compact cache with room for gist_capacity gists. */
+int32_t gsa_compact_slots(const gsa_layout* layout, int32_t gist_capacity);
+
+/* Host only.  Gists among the first seq_len positions (the capacity needed). */
+int32_t gsa_compact_gists(const gsa_layout* layout, int32_t seq_len);
+
+/* Writes the K/V of the tokens at positions [pos0, pos0 + n) -- k_new, v_new
+ * [B, n, Hkv, d] by strides -- into their slots of the compact caches.  Raw
+ * tokens more than W positions before the last one are skipped (no later
+ * query can see them).  Positions must be appended in order, each once. */
+gsa_status gsa_compact_append(const gsa_layout* layout, gsa_tensor k_new, gsa_tensor v_new, int32_t B,
+                              int32_t Hkv, int32_t d, int32_t pos0, int32_t n, gsa_tensor k_cache,
+                              gsa_tensor v_cache, int32_t gist_capacity, void* stream);
+
+/* Decode of one query per sequence at position `pos` (its own K/V already
+ * appended) over compact caches: softmax attention to the sinks, the gists at
+ * or before pos and the raw tokens of its window -- the fixed layout's
+ * visible set -- split over many workgroups per (batch, KV head), merged by
+ * the last one.  q, o [B, Hq, d]; lse nullable float [B, Hq]; ws a workspace
+ * of gsa_compact_decode_workspace_bytes(), 256-byte aligned, zero-filled
+ * before first use (its counters are left at zero by every call).
+ * Requires bf16 q and caches, d in {64, 128}, Hq/Hkv <= 16. */
+gsa_status gsa_compact_decode(const gsa_layout* layout, gsa_tensor q, gsa_tensor k_cache, gsa_tensor v_cache,
+                              gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                              int32_t pos, int32_t gist_capacity, float scale, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Host only.  Workspace bytes gsa_compact_decode needs (0 if invalid). */
+size_t gsa_compact_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
+                                          int32_t d, int32_t pos);
+
 /* Host only.  Workspace bytes gsa_attn_decode needs for these sizes. */
 size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t d, int32_t kv_len);

@@ -111,3 +111,15 @@ def test_invalid_arguments_rejected_before_launch(lib):
     t32 = gsa.Tensor(16, gsa.GSA_F32, 0, 0, 0, 0)
     assert lib.gsa_attn_decode(ctypes.byref(dl), t32, t32, t32, t32, None, 1, 4, 1, 128, 50, 16,
                                None, 0.1, 16, 1 << 30, None) == gsa.GSA_EUNSUPPORTED
+
+
+def test_compact_sizes(lib):
+    """Slots = sinks + gist capacity + max(window, 1); gists counted as the
+    layout places them (ratio 4 at 32K raw tokens: 8192 gists)."""
+    lay = dict(n_sink=128, chunk_len=4, gists=1, window=128, top_k=0)
+    assert gsa.compact_slots(lay, 8192) == 128 + 8192 + 128
+    assert gsa.compact_gists(lay, 128 + 8192 * 5 + 1) == 8192
+    assert gsa.compact_gists(lay, 128 + 3 * 5 + 4) == 3
+    assert gsa.compact_gists(lay, 128 + 3 * 5 + 5) == 4
+    assert gsa.compact_slots(dict(n_sink=0, chunk_len=3, gists=2, window=0, top_k=0), 5) == 0 + 5 + 1
+    assert gsa.compact_slots(dict(n_sink=1, chunk_len=3, gists=1, window=4, top_k=1), 5) == -1

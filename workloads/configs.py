@@ -109,5 +109,16 @@ HIER_DECODE = Workload(
     plant_chunks=16, plant_groups=8,
     note="gist-of-gist decode: top-8 groups, then top-16 chunks inside them")
 
+# Next-step workloads (built after the five above; see the design notes).
+# Fixed-layout decode over a compacted cache (raw tokens outside the window
+# removed): the UniGist setting of the 8B attention shape at ratio 4, 128 sinks,
+# window 128, 32768 raw tokens before the query.
+COMPACT_DECODE = Workload(
+    name="unigist_compact_decode_b16_8b_ratio4_32k", kind="decode", dtype="bf16",
+    batch=16, hq=32, hkv=8, d=128, n_sink=128, chunk_len=4, gists=1, window=128,
+    top_k=0, n_chunks=8192,
+    note="one query per sequence over a cache of sinks + gists + a 128-slot ring of raws")
+
 ALL = [TINY_PREFILL_F32, LLAMA3B_K0_PREFILL, LLAMA8B_K0_PREFILL, SELECTIVE_DECODE, HIER_DECODE]
-BY_NAME = {w.name: w for w in ALL}
+NEXT = [COMPACT_DECODE]
+BY_NAME = {w.name: w for w in ALL + NEXT}
