@@ -329,6 +329,81 @@ def run_decode(w, args, torch, gsa, copies=4):
             "separate_calls_ms_per_step": round(ms_sep, 5)}
 
 
+def unfolded_edges(w, sel: np.ndarray) -> int:
+    """Visible pairs summed over (batch, KV head) of a single-level layout with
+    the given selection [B, Hkv, L, k]: the fixed part per row plus the raws of
+    each chosen chunk before the row's window."""
+    S, c, g, W1, L = w.n_sink, w.chunk_len, w.gists, max(w.window, 1), w.seq_len
+    P = c + g
+    i = np.arange(L, dtype=np.int64)
+    lo = np.maximum(0, i - W1 + 1)
+    base = fixed_layout_edges(w)
+    st = S + sel.astype(np.int64) * P
+    extra = np.clip(lo[None, None, :, None] - st, 0, c)
+    extra = np.where(sel >= 0, extra, 0)
+    return int(base * sel.shape[0] * sel.shape[1] + extra.sum())
+
+
+def run_unfolded(w, args, torch, gsa, q, k, v):
+    """Selective-unfolding prefill: one step = gsa_select_prefill + the fixed
+    part's table + gsa_attn_prefill_unfolded (unfold kernel, then the MFMA
+    prefill starting from its partials)."""
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    bm, bn = gsa.prefill_tile(torch.bfloat16, w.d)
+    fixed = dict(w.layout, top_k=0)
+    nqt, nkt = gsa.table_dims(fixed, w.seq_len, w.seq_len, bm, bn)
+    tables = (torch.empty((1, nqt, nkt), dtype=torch.int8, device=dev),
+              torch.empty((1, nqt), dtype=torch.int32, device=dev),
+              torch.empty((1, nqt, nkt), dtype=torch.int32, device=dev))
+    sel = torch.empty((w.batch, w.hkv, w.seq_len, w.top_k), dtype=torch.int32, device=dev)
+    o = torch.empty((w.batch, w.seq_len, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(gsa.prefill_unfolded_workspace_bytes(w.batch, w.hq, w.d, w.seq_len), dtype=torch.uint8,
+                     device=dev)
+    scale = 1 / math.sqrt(w.d)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gsa.select_prefill(w.layout, tq, tk, w.seq_len, 0, scale, out=sel)
+        if ev is not None:
+            ev[1].record()
+        gsa.build_layout(fixed, w.seq_len, 0, w.seq_len, bm, bn, out=tables)
+        if ev is not None:
+            ev[2].record()
+        gsa.attn_prefill_unfolded(w.layout, tq, tk, tv, sel, tables, bm, bn, 0, scale, workspace=ws,
+                                  out=(o, None))
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(2, args.steps // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    sl = sel.cpu().numpy()
+    alg = 4.0 * w.d * unfolded_edges(w, sl) * (w.hq // w.hkv)
+    S, c, g = w.n_sink, w.chunk_len, w.gists
+    ncand = _counts(S, c, g, np.arange(w.seq_len))[0].astype(np.int64)
+    sel_flops = 2.0 * w.d * float(ncand.sum()) * w.batch * w.hkv
+    del tq, tk, tv, o, ws
+    return {"workload": w.name, "ms_per_step": round(wall, 4), "select_ms": round(sel_ms, 4),
+            "unfold_and_prefill_ms": round(att_ms, 4), "algorithmic_flops": alg,
+            "tflops_algorithmic_step": round(alg / (wall * 1e-3) / 1e12, 2),
+            "tflops_algorithmic_attention": round(alg / (att_ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak_attention": round(alg / (att_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "selection_screen_flops": sel_flops,
+            "selection_tflops": round(sel_flops / (sel_ms * 1e-3) / 1e12, 2),
+            "kernels": "k_select_prefill; k_build_table; k_unfold + k_prefill_mfma (init from the unfold partial)"}
+
+
 def run_compact(w, args, torch, gsa, copies=2):
     """Fixed-layout decode over a compacted cache (sinks + gists + a window
     ring of raws): K/V of the whole sequence are drawn on the GPU (seeded),
@@ -434,6 +509,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-8b", action="store_true")
+    ap.add_argument("--no-unfold", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--pass-workload", default="llama3b_gqa24x8_ratio4_k0_prefill_32k")
@@ -492,6 +568,14 @@ def main():
         del q, k, v
         log(f"prefill {w8.name}: {p8['ms_per_step']:.3f} ms/step, kernel {p8['kernel_ms']:.3f} ms")
         out["prefill"] = [p8]
+    if not args.no_unfold:
+        wu = configs.LLAMA3B_K16_PREFILL
+        q, k, v = inputs.prefill_inputs(wu, seed=1)
+        pu = run_unfolded(wu, args, torch, gsa, q, k, v)
+        del q, k, v
+        log(f"prefill {wu.name}: {pu['ms_per_step']:.3f} ms/step (select {pu['select_ms']:.3f} ms, "
+            f"unfold + prefill {pu['unfold_and_prefill_ms']:.3f} ms)")
+        out.setdefault("prefill", []).append(pu)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if not args.no_decode:

@@ -45,7 +45,8 @@ EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_
            "gsa_attn_prefill", "gsa_prefill_tile", "gsa_attn_decode", "gsa_attn_decode_noalloc",
            "gsa_decode_workspace_bytes", "gsa_decode_step", "gsa_decode_step_workspace_bytes",
            "gsa_compact_slots", "gsa_compact_gists", "gsa_compact_append", "gsa_compact_decode",
-           "gsa_compact_decode_workspace_bytes", "gsa_status_str", "gsa_last_error")
+           "gsa_compact_decode_workspace_bytes", "gsa_select_prefill", "gsa_attn_prefill_unfolded",
+           "gsa_prefill_unfolded_workspace_bytes", "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -88,6 +89,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                        V, ctypes.c_size_t, V]
     lib.gsa_compact_decode_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
     lib.gsa_compact_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_select_prefill.argtypes = [LP, Tensor, Tensor, I32, I32, I32, I32, I32, I32, I32, F, V, V]
+    lib.gsa_attn_prefill_unfolded.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32,
+                                              I32, I32, V, V, V, V, I32, I32, F, V, ctypes.c_size_t, V]
+    lib.gsa_prefill_unfolded_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.gsa_prefill_unfolded_workspace_bytes.restype = ctypes.c_size_t
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
@@ -95,7 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in EXPORTS:
         if name not in ("gsa_score_columns", "gsa_decode_workspace_bytes", "gsa_status_str",
                         "gsa_last_error", "gsa_decode_step_workspace_bytes", "gsa_compact_slots",
-                        "gsa_compact_gists", "gsa_compact_decode_workspace_bytes"):
+                        "gsa_compact_gists", "gsa_compact_decode_workspace_bytes",
+                        "gsa_prefill_unfolded_workspace_bytes"):
             getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -372,3 +379,46 @@ def compact_decode(layout: dict, q, k_cache, v_cache, pos: int, gist_capacity: i
 def compact_decode_workspace_bytes(layout: dict, B: int, Hq: int, Hkv: int, d: int, pos: int) -> int:
     return int(load_library().gsa_compact_decode_workspace_bytes(ctypes.byref(make_layout(layout)), B, Hq, Hkv,
                                                                  d, pos))
+
+
+def select_prefill(layout: dict, q, k, seq_len: int, q_begin: int = 0, scale: float | None = None, out=None):
+    """Top-k chunks of every query row ``q [B, Nq, Hq, d]`` over keys
+    ``k [B, L, Hkv, d]`` (single level, one gist per chunk); returns sel."""
+    lib = load_library()
+    B, Nq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    sel = out if out is not None else torch.empty((B, Hkv, Nq, int(layout["top_k"])), dtype=torch.int32,
+                                                  device=q.device)
+    _check(lib.gsa_select_prefill(ctypes.byref(make_layout(layout)), _bthd(q), _bthd(k), B, Hq, Hkv, d, seq_len,
+                                  q_begin, Nq, float(scale), sel.data_ptr(), _stream()))
+    return sel
+
+
+def prefill_unfolded_workspace_bytes(B: int, Hq: int, d: int, q_len: int) -> int:
+    return int(load_library().gsa_prefill_unfolded_workspace_bytes(B, Hq, d, q_len))
+
+
+def attn_prefill_unfolded(layout: dict, q, k, v, sel, fixed_tables, block_m: int, block_n: int, q_begin: int = 0,
+                          scale: float | None = None, out_dtype=torch.float32, want_lse: bool = True,
+                          workspace=None, out=None):
+    """Prefill with selective unfolding: ``fixed_tables`` is the (table,
+    tile_cnt, tile_list) of the same layout with top_k = 0."""
+    lib = load_library()
+    B, Nq, Hq, d = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(max(prefill_unfolded_workspace_bytes(B, Hq, d, Nq), 256), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        o = torch.empty((B, Nq, Hq, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    else:
+        o, lse = out
+    table, cnt, lst = fixed_tables
+    _check(lib.gsa_attn_prefill_unfolded(ctypes.byref(make_layout(layout)), _bthd(q), _bthd(k), _bthd(v),
+                                         _bthd(o), _ptr(lse), B, Hq, Hkv, d, L, q_begin, Nq, sel.data_ptr(),
+                                         table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m, block_n,
+                                         float(scale), workspace.data_ptr(), workspace.numel(), _stream()))
+    return o, lse

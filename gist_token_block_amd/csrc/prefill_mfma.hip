@@ -78,7 +78,10 @@ template <> struct OutStore<unsigned short> {
 
 // LSE: also write the log-sum-exp, normalised by a separate fp32 sum of the
 // unrounded probabilities (O keeps the sum of the bf16 P that feeds it).
-template <int D, typename TO, bool LSE>
+// INIT: each row starts from a softmax partial over keys outside the table
+// (init [B, q_len, Hq, D + 3]: unnormalised O, max in log2 units, sums) --
+// the raw tokens its chosen chunks unfold -- instead of from zero.
+template <int D, typename TO, bool LSE, bool INIT>
 __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     int64_t osb, int64_t ost, int64_t osh, float* __restrict__ lse, int Hq, int Hkv, int q_begin,
     int q_len, int nqt, const int* __restrict__ sel, const int* __restrict__ selg,
     const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
-    const int* __restrict__ tile_list, float c2, int fixed, int total) {
+    const int* __restrict__ tile_list, float c2, int fixed, int total, const float* __restrict__ init) {
   using C = Cfg<D>;
   // Double-buffered K and V tiles as four separate arrays, indexed only
   // statically (the tile loop is unrolled by two): the compiler can then tell
@@ -157,6 +160,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
   for (int mt = 0; mt < C::MT; ++mt) oacc[mt] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
   float l_ex = 0.f;   // LSE only: sum of the unrounded P
+  if constexpr (INIT) {
+    if (rvalid) {
+      // O^T accumulator element j of tile mt holds d = 32 mt + 8 (j / 4) + 4 h2 + j % 4;
+      // the two lanes of a query share the max and split the sums (h2 = 0 holds them)
+      const float* ip = init + (((size_t)b * q_len + r) * Hq + hq) * (D + 3);
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(ip + 32 * mt + 8 * jj + 4 * h2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) oacc[mt][4 * jj + e] = w[e];
+        }
+      m_run = ip[D];
+      l_run = h2 == 0 ? ip[D + 1] : 0.f;
+      l_ex = h2 == 0 ? ip[D + 2] : 0.f;
+    }
+  }
 
   // Staging: wave load `wi` (0 .. 4*NIW-1) fills key rows [wi*RPI, wi*RPI+RPI)
   // of a tile; lane -> row wi*RPI + lane / PPR, LDS slot lane % PPR, which
@@ -475,12 +496,12 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
     if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
     const float c2 = scale * kLog2e;
 #define GSA_MFMA1(D, TO, LSE)                                                                        \
-  hipLaunchKernelGGL((k_prefill_mfma<D, TO, LSE>), dim3((unsigned)total), dim3(kThreads), 0, s, l,    \
+  hipLaunchKernelGGL((k_prefill_mfma<D, TO, LSE, false>), dim3((unsigned)total), dim3(kThreads), 0, s, l, \
                      (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                \
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr,    \
                      o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, nqt, sel,      \
-                     sel_groups, table, tile_cnt, tile_list, c2, (int)fixed, (int)total)
+                     sel_groups, table, tile_cnt, tile_list, c2, (int)fixed, (int)total, nullptr)
 #define GSA_MFMA(D, TO)             \
   if (lse) GSA_MFMA1(D, TO, true);  \
   else GSA_MFMA1(D, TO, false)
@@ -498,4 +519,80 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
   if (block_n > 256) return fail(GSA_EUNSUPPORTED, "block_n %d > 256 on the row-wave path", block_n);
   return launch_prefill_rowwave(l, d, q, k, v, o, lse, B, Hq, Hkv, q_begin, q_len, block_m, nqt, sel,
                                 sel_groups, table, tile_cnt, tile_list, scale, fixed, s);
+}
+
+namespace gsa {
+gsa_status launch_unfold(const Lay& l, int d, const gsa_tensor& q, const gsa_tensor& k, const gsa_tensor& v, int B,
+                         int Hq, int Hkv, int q_begin, int q_len, const int* sel, float scale, float* part,
+                         hipStream_t st);
+}
+
+extern "C" size_t gsa_prefill_unfolded_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t q_len) {
+  if (B < 1 || Hq < 1 || d < 1 || q_len < 0) return 0;
+  return (size_t)B * q_len * Hq * (d + 3) * sizeof(float);
+}
+
+extern "C" gsa_status gsa_attn_prefill_unfolded(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                                gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv,
+                                                int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                                                const int32_t* sel, const int8_t* table, const int32_t* tile_cnt,
+                                                const int32_t* tile_list, int32_t block_m, int32_t block_n,
+                                                float scale, void* ws, size_t ws_bytes, void* stream) {
+  Lay l;
+  gsa_status st = make_lay(layout, seq_len, block_n, &l);
+  if (st != GSA_OK) return st;
+  if (l.G2 != 0) return fail(GSA_EUNSUPPORTED, "unfolded prefill takes one level");
+  if (l.k < 1) return fail(GSA_EINVAL, "top_k must be >= 1 (the fixed layout needs no unfolding)");
+  gsa_layout fixed_layout = *layout;
+  fixed_layout.top_k = 0;
+  Lay lf;
+  if ((st = make_lay(&fixed_layout, seq_len, block_n, &lf)) != GSA_OK) return st;
+  if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
+  if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
+  if ((st = check_tensor("v", v, d)) != GSA_OK) return st;
+  if ((st = check_tensor("o", o, d)) != GSA_OK) return st;
+  if (q.dtype != GSA_BF16 || k.dtype != GSA_BF16 || v.dtype != GSA_BF16)
+    return fail(GSA_EUNSUPPORTED, "unfolded prefill takes bf16 q, k, v");
+  if (o.dtype != GSA_F32 && o.dtype != GSA_BF16) return fail(GSA_EINVAL, "o dtype must be F32 or BF16");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(GSA_EINVAL, "bad head counts B=%d Hq=%d Hkv=%d", B, Hq, Hkv);
+  if (d != 64 && d != 128) return fail(GSA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (!(scale > 0.f)) return fail(GSA_EINVAL, "scale must be > 0");
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (block_m != kBM || block_n != kBN)
+    return fail(GSA_EINVAL, "the unfolded prefill needs the %dx%d table of the fixed layout (got %dx%d)", kBM, kBN,
+                block_m, block_n);
+  if (!sel) return fail(GSA_EINVAL, "sel is NULL");
+  if (!table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "table pointers are NULL");
+  const size_t need = gsa_prefill_unfolded_workspace_bytes(B, Hq, d, q_len);
+  if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
+  if (q_len == 0) return GSA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  float* part = (float*)ws;
+  if ((st = launch_unfold(l, d, q, k, v, B, Hq, Hkv, q_begin, q_len, sel, scale, part, s)) != GSA_OK) return st;
+  const int nqt = (q_len + kBM - 1) / kBM;
+  const long long total = (long long)B * Hkv * nqt * (Hq / Hkv);
+  if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
+  const float c2 = scale * kLog2e;
+#define GSA_MFMA_I(D, TO, LSE)                                                                        \
+  hipLaunchKernelGGL((k_prefill_mfma<D, TO, LSE, true>), dim3((unsigned)total), dim3(kThreads), 0, s, lf, \
+                     (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                \
+                     (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                \
+                     (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr,    \
+                     o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, nqt, nullptr,  \
+                     nullptr, table, tile_cnt, tile_list, c2, 1, (int)total, part)
+#define GSA_MFMA_I2(D, TO)              \
+  if (lse) GSA_MFMA_I(D, TO, true);     \
+  else GSA_MFMA_I(D, TO, false)
+  if (d == 128) {
+    if (o.dtype == GSA_F32) GSA_MFMA_I2(128, float);
+    else GSA_MFMA_I2(128, unsigned short);
+  } else {
+    if (o.dtype == GSA_F32) GSA_MFMA_I2(64, float);
+    else GSA_MFMA_I2(64, unsigned short);
+  }
+#undef GSA_MFMA_I2
+#undef GSA_MFMA_I
+  return launch_status("gsa_attn_prefill_unfolded");
 }

@@ -153,6 +153,44 @@ gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k
                             const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m,
                             int32_t block_n, float scale, void* stream);
 
+/* Top-k selection for many query rows at once (SSA abstract: score the
+ * chunks against their gist keys only, keep the k best), the same result as
+ * gsa_score_select up to fp32 rounding of the scores: per 128 query rows and
+ * KV head, one MFMA pass over the gist stream screens candidates with the
+ * group's mean query rounded to bf16, each row keeps its best top_k + 4 or
+ * more, and those are ranked by their fp32 scores.  Single level with one
+ * gist per chunk, bf16, d in {64, 128}, 1 <= top_k <= 28.
+ *   q    [B, q_len, Hq, d]; k [B, seq_len, Hkv, d] (by strides)
+ *   sel  int32 [B, Hkv, q_len, top_k] (out), ascending, -1 padded */
+gsa_status gsa_select_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                              float scale, int32_t* sel, void* stream);
+
+/* Prefill with selective unfolding at scale (SSA abstract; GSA abstract:
+ * restore the raw chunks of the selected gists).  A query's visible keys are
+ * the fixed part (sinks, earlier gists, window: UniGist summary, Approach)
+ * plus the raw tokens of its top_k chosen chunks that lie before its window.
+ * The unfolded raws of each (query, KV group) are attended first into a
+ * softmax partial per query head (workspace), and the MFMA prefill over the
+ * fixed part then starts each row from that partial.
+ *   layout  single level, top_k >= 1
+ *   sel     int32 [B, Hkv, q_len, top_k]: gsa_select_prefill's (or
+ *           gsa_score_select's) output
+ *   table, tile_cnt, tile_list  the fixed part's table: gsa_build_layout on
+ *           the same layout with top_k = 0, n_tables = 1, the MFMA tile shape
+ *   ws      workspace of gsa_prefill_unfolded_workspace_bytes(), 256-byte
+ *           aligned (no initialisation needed)
+ * bf16 q, k, v; o F32 or BF16; lse nullable [B, Hq, q_len]; d in {64, 128}. */
+gsa_status gsa_attn_prefill_unfolded(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                     gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                     int32_t seq_len, int32_t q_begin, int32_t q_len, const int32_t* sel,
+                                     const int8_t* table, const int32_t* tile_cnt, const int32_t* tile_list,
+                                     int32_t block_m, int32_t block_n, float scale, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/* Host only.  Workspace bytes of gsa_attn_prefill_unfolded. */
+size_t gsa_prefill_unfolded_workspace_bytes(int32_t B, int32_t Hq, int32_t d, int32_t q_len);
+
 /* Host only.  Tile shape the prefill kernel for (dtype, d) expects. */
 gsa_status gsa_prefill_tile(int32_t dtype, int32_t d, int32_t* block_m, int32_t* block_n);
 

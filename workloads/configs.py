@@ -119,6 +119,14 @@ COMPACT_DECODE = Workload(
     top_k=0, n_chunks=8192,
     note="one query per sequence over a cache of sinks + gists + a 128-slot ring of raws")
 
+# Selective unfolding at prefill scale: the 3B shape's 32K layout with every
+# query unfolding its 16 best chunks.
+LLAMA3B_K16_PREFILL = Workload(
+    name="llama3b_gqa24x8_ratio4_k16_prefill_32k", kind="prefill", dtype="bf16",
+    batch=1, hq=24, hkv=8, d=128, n_sink=128, chunk_len=4, gists=1, window=128,
+    top_k=16, n_chunks=8192,
+    note="3B attention shape, 32K raw tokens, per-query top-16 unfolding")
+
 ALL = [TINY_PREFILL_F32, LLAMA3B_K0_PREFILL, LLAMA8B_K0_PREFILL, SELECTIVE_DECODE, HIER_DECODE]
-NEXT = [COMPACT_DECODE]
+NEXT = [COMPACT_DECODE, LLAMA3B_K16_PREFILL]
 BY_NAME = {w.name: w for w in ALL + NEXT}
