@@ -14,6 +14,11 @@ namespace gsa {
 __device__ inline bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
+// The same order evaluated without short-circuit (no branches in unrolled
+// per-lane loops).
+__device__ inline bool better_nb(float s1, int i1, float s2, int i2) {
+  return (bool)((unsigned)(s1 > s2) | ((unsigned)(s1 == s2) & (unsigned)(i1 < i2)));
+}
 
 // Value of lane ^ j for a constant j (the networks below unroll fully):
 // DPP quad permutes for 1 and 2, a row rotation by 8 for 8 (a rotation by half

@@ -42,6 +42,21 @@ template <int D> struct SCfg {
 };
 template <int D> __device__ inline int sswz(int r) { return r & (D / 8 - 1); }
 
+// (score, id) as one unsigned key ordered like (score desc, id asc): the float
+// bits made monotone (negative scores flipped whole, positive ones get the
+// sign bit) above ~id.  Scores are never NaN here; -inf maps above 0, so the
+// key 0 stands for an empty slot.
+__device__ inline unsigned long long make_key(float s, int id) {
+  const unsigned u = __float_as_uint(s);
+  const unsigned m = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)m << 32) | (unsigned)~id;
+}
+__device__ inline float key_score(unsigned long long k) {
+  const unsigned m = (unsigned)(k >> 32);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
+__device__ inline int key_id(unsigned long long k) { return (int)~(unsigned)k; }
+
 template <int D, int KA>
 __global__ __launch_bounds__(kThreads, 2) void k_select_prefill(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
@@ -116,16 +131,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_select_prefill(
     asm volatile("" : "+v"(qk_off[ks]));
   }
 
-  // the lane's survivors (unsorted) and its current worst
-  float ls[KA];
-  int li[KA];
+  // the lane's survivors as 64-bit keys, ascending (key[0] is the worst):
+  // high word the order-preserving bits of the score, low word ~id, so a
+  // larger key is a better (score desc, id asc) candidate; key 0 is empty
+  unsigned long long key[KA];
 #pragma unroll
-  for (int j = 0; j < KA; ++j) {
-    ls[j] = -__builtin_inff();
-    li[j] = INT_MAX;
-  }
-  float wmin_s = -__builtin_inff();
-  int wmin_i = INT_MAX, wmin_j = 0;
+  for (int j = 0; j < KA; ++j) key[j] = 0ull;
 
   if (ntile > 0) fetch(0, K0);
   auto tile = [&](int t, const unsigned short* Kb, unsigned short* Kn) {
@@ -140,46 +151,44 @@ __global__ __launch_bounds__(kThreads, 2) void k_select_prefill(
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
     }
-    // value slot x = 16 half + j is candidate 64 t + 32 half + 8 (j / 4) + 4 h2 + j % 4
+    // value slot x = 16 half + j is candidate 64 t + 32 half + 8 (j / 4) + 4 h2 + j % 4.
+    // The mask marks a superset of the candidates that beat the worst
+    // survivor (every candidate while a slot is empty, else score >= the
+    // worst's; a NaN score, which ranks as -inf, cannot beat a full set);
+    // each marked one is re-checked exactly before it is inserted.
+    const float wmin_s = key_score(key[0]);
+    const bool fill = key[0] == 0ull || wmin_s == -__builtin_inff();
     unsigned mask = 0;
 #pragma unroll
     for (int x = 0; x < 32; ++x) {
-      const int j = x & 15;
-      const int id = t * kBN + 32 * (x >> 4) + 8 * (j >> 2) + 4 * h2 + (j & 3);
-      const float v = nan_to_neg_inf(x < 16 ? s0[j] : s1[j]);
+      const float v = x < 16 ? s0[x & 15] : s1[x & 15];
       sc[wave][x][lane] = v;
-      mask |= (unsigned)(rvalid && id < ncand && better(v, id, wmin_s, wmin_i)) << x;
+      mask |= (unsigned)(v >= wmin_s) << x;
     }
-    // replace the worst survivor once per marked candidate (re-checked, as
-    // the worst rises)
-    while (__ballot(mask != 0u)) {
-      if (mask) {
-        const int x = __builtin_ctz(mask);
-        mask &= mask - 1u;
-        const int j = x & 15;
-        const int id = t * kBN + 32 * (x >> 4) + 8 * (j >> 2) + 4 * h2 + (j & 3);
-        const float v = sc[wave][x][lane];
-        if (better(v, id, wmin_s, wmin_i)) {
+    if (fill) mask = 0xffffffffu;
+    if (!rvalid) mask = 0u;
+    const int idb = t * kBN + 4 * h2;
+    // one sorted insertion per marked candidate, straight-line in every lane
+    auto insert_next = [&]() {
+      const bool has = mask != 0u;
+      const int x = has ? __builtin_ctz(mask) : 0;
+      mask &= mask - 1u;
+      const int j = x & 15;
+      const int id = idb + 32 * (x >> 4) + 8 * (j >> 2) + (j & 3);
+      const unsigned long long c = (has && id < ncand) ? make_key(nan_to_neg_inf(sc[wave][x][lane]), id) : 0ull;
+      bool bnext = c > key[0];
 #pragma unroll
-          for (int e = 0; e < KA; ++e) {
-            if (e == wmin_j) {
-              ls[e] = v;
-              li[e] = id;
-            }
-          }
-          wmin_s = ls[0];
-          wmin_i = li[0];
-          wmin_j = 0;
-#pragma unroll
-          for (int e = 1; e < KA; ++e) {
-            if (better(wmin_s, wmin_i, ls[e], li[e])) {
-              wmin_s = ls[e];
-              wmin_i = li[e];
-              wmin_j = e;
-            }
-          }
-        }
+      for (int e = 0; e < KA - 1; ++e) {
+        const bool be = bnext;
+        bnext = c > key[e + 1];
+        key[e] = bnext ? key[e + 1] : (be ? c : key[e]);
       }
+      key[KA - 1] = bnext ? c : key[KA - 1];
+    };
+    // two per trip (the second is a no-op for a lane with nothing left)
+    while (__ballot(mask != 0u)) {
+      insert_next();
+      insert_next();
     }
   };
   for (int t = 0; t < ntile; t += 2) {
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_select_prefill(
     pool_s = pool_own + wave * 2048 + n * 64;
   }
 #pragma unroll
-  for (int c = 0; c < KA; ++c) pool_i[h2 * KA + c] = li[c];
+  for (int c = 0; c < KA; ++c) pool_i[h2 * KA + c] = key[c] ? key_id(key[c]) : INT_MAX;
   __builtin_amdgcn_wave_barrier();
   // fp32 qbar over this lane's half of the dimensions, d = (D / 2) h2 + 0 .. D / 2 - 1
   float qb[D / 2];

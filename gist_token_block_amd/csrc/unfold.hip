@@ -29,11 +29,12 @@ constexpr int kWaves = 4;
 constexpr int kMaxKeys = 64;       // unfolded raws handled per pass of a wave
 constexpr int kMaxG = 16;
 
-// One wave per (batch, KV head, query row), grid-stride.  Lane j of a pass
+// One wave per (batch, KV head, query row), grid-stride; MG bounds the query
+// heads per KV head (the per-head registers are sized by it).  Lane j of a pass
 // owns unfolded key j: it computes that key's logits for the group's heads; the
 // probabilities go through LDS, and each lane then accumulates two output
 // dimensions over the pass's keys.
-template <int D>
+template <int D, int MG>
 __global__ __launch_bounds__(64 * kWaves) void k_unfold(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
@@ -41,8 +42,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
     int q_begin, int q_len, const int* __restrict__ sel, float c2, float* __restrict__ part) {
   constexpr int PS = D + kUnfoldExtra;
   constexpr int DPL = D / 64;      // output dimensions per lane
-  __shared__ float qs[kWaves][kMaxG][D];
-  __shared__ float ps[kWaves][kMaxG][kMaxKeys];
+  __shared__ float qs[kWaves][MG][D];
+  __shared__ float ps[kWaves][MG][kMaxKeys];
   __shared__ int kpos[kWaves][kMaxKeys];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = Hq / Hkv;
@@ -77,9 +78,9 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
       const int hd = x / D, dd = x - hd * D;
       qs[wave][hd][dd] = bf16_to_f32(q[b * qsb + (int64_t)r * qst + (int64_t)(h * G + hd) * qsh + dd]);
     }
-    float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][DPL];
+    float m_run[MG], l_run[MG], acc[MG][DPL];
 #pragma unroll
-    for (int hd = 0; hd < kMaxG; ++hd) {
+    for (int hd = 0; hd < MG; ++hd) {
       m_run[hd] = kNegBig;
       l_run[hd] = 0.f;
 #pragma unroll
@@ -95,32 +96,43 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
       }
       kpos[wave][lane] = p;
       __builtin_amdgcn_wave_barrier();
-      // logits of key lane for every head of the group
-      float lg[kMaxG];
+      // logits of key lane for every head of the group: the whole K row is
+      // loaded first (all its pieces in flight), then dotted with the group's
+      // query rows read from LDS as broadcasts
+      float lg[MG];
 #pragma unroll
-      for (int hd = 0; hd < kMaxG; ++hd) lg[hd] = 0.f;
-      if (p >= 0) {
-        const unsigned short* krow = k + b * ksb + (int64_t)p * kst + h * ksh;
-        for (int d0 = 0; d0 < D; d0 += 8) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(krow + d0);
-          float kv[8];
+      for (int hd = 0; hd < MG; ++hd) lg[hd] = 0.f;
+      {
+        u32x4 kr[D / 8];
+        const unsigned short* krow = k + b * ksb + (int64_t)imax(p, 0) * kst + h * ksh;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv[2 * e] = lo_bf16(w[e]);
-            kv[2 * e + 1] = hi_bf16(w[e]);
-          }
+        for (int c8 = 0; c8 < D / 8; ++c8)
+          kr[c8] = p >= 0 ? *reinterpret_cast<const u32x4*>(krow + 8 * c8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int hd = 0; hd < kMaxG; ++hd) {
-            if (hd < G) {
+        for (int hd = 0; hd < MG; ++hd) {
+          if (hd < G) {
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) lg[hd] = fmaf(qs[wave][hd][d0 + e], kv[e], lg[hd]);
+            for (int c8 = 0; c8 < D / 8; ++c8) {
+              const f32x4 qa = *reinterpret_cast<const f32x4*>(&qs[wave][hd][8 * c8]);
+              const f32x4 qb = *reinterpret_cast<const f32x4*>(&qs[wave][hd][8 * c8 + 4]);
+              const u32x4 w = kr[c8];
+              a0 = fmaf(qa[0], lo_bf16(w[0]), a0);
+              a1 = fmaf(qa[1], hi_bf16(w[0]), a1);
+              a0 = fmaf(qa[2], lo_bf16(w[1]), a0);
+              a1 = fmaf(qa[3], hi_bf16(w[1]), a1);
+              a0 = fmaf(qb[0], lo_bf16(w[2]), a0);
+              a1 = fmaf(qb[1], hi_bf16(w[2]), a1);
+              a0 = fmaf(qb[2], lo_bf16(w[3]), a0);
+              a1 = fmaf(qb[3], hi_bf16(w[3]), a1);
             }
+            lg[hd] = a0 + a1;
           }
         }
       }
       // online softmax per head over this pass's keys (base 2)
 #pragma unroll
-      for (int hd = 0; hd < kMaxG; ++hd) {
+      for (int hd = 0; hd < MG; ++hd) {
         if (hd < G) {
           const float s = p >= 0 ? lg[hd] * c2 : -__builtin_inff();
           float mx = s;
@@ -140,25 +152,37 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
         }
       }
       __builtin_amdgcn_wave_barrier();
-      // PV: lane owns output dimensions lane * DPL .. + DPL - 1
+      // PV: lane owns output dimensions lane * DPL .. + DPL - 1; every V load
+      // of the pass is issued before the products
       const int nkp = imin(kMaxKeys, nk - k0);
-      for (int j = 0; j < nkp; ++j) {
-        const int pj = kpos[wave][j];
-        const unsigned short* vrow = v + b * vsb + (int64_t)pj * vst + h * vsh + lane * DPL;
-        float vv[DPL];
-        if constexpr (DPL == 2) {
-          const unsigned w = *reinterpret_cast<const unsigned*>(vrow);
-          vv[0] = lo_bf16(w);
-          vv[1] = hi_bf16(w);
-        } else {
-          vv[0] = bf16_to_f32(vrow[0]);
+      unsigned vw[kMaxKeys];
+#pragma unroll
+      for (int j = 0; j < kMaxKeys; ++j) {
+        vw[j] = 0u;
+        if (j < nkp) {
+          const int pj = kpos[wave][j];
+          const unsigned short* vrow = v + b * vsb + (int64_t)pj * vst + h * vsh + lane * DPL;
+          if constexpr (DPL == 2) vw[j] = *reinterpret_cast<const unsigned*>(vrow);
+          else vw[j] = (unsigned)vrow[0] << 16;
         }
+      }
 #pragma unroll
-        for (int hd = 0; hd < kMaxG; ++hd) {
-          if (hd < G) {
-            const float pr = ps[wave][hd][j];
+      for (int j4 = 0; j4 < kMaxKeys; j4 += 4) {
+        if (j4 < nkp) {
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[hd][e] = fmaf(pr, vv[e], acc[hd][e]);
+          for (int hd = 0; hd < MG; ++hd) {
+            if (hd < G) {
+              const f32x4 pr = *reinterpret_cast<const f32x4*>(&ps[wave][hd][j4]);
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                if constexpr (DPL == 2) {
+                  acc[hd][0] = fmaf(pr[jj], lo_bf16(vw[j4 + jj]), acc[hd][0]);
+                  acc[hd][1] = fmaf(pr[jj], hi_bf16(vw[j4 + jj]), acc[hd][1]);
+                } else {
+                  acc[hd][0] = fmaf(pr[jj], hi_bf16(vw[j4 + jj]), acc[hd][0]);
+                }
+              }
+            }
           }
         }
       }
@@ -166,7 +190,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
     }
     // the partial of each head: unnormalised O, max (log2 units), sums
 #pragma unroll
-    for (int hd = 0; hd < kMaxG; ++hd) {
+    for (int hd = 0; hd < MG; ++hd) {
       if (hd < G) {
         float* dst = part + (((size_t)b * q_len + r) * Hq + h * G + hd) * PS;
 #pragma unroll
@@ -197,15 +221,22 @@ gsa_status launch_unfold(const Lay& l, int d, const gsa_tensor& q, const gsa_ten
   const long long want = (items + kWaves - 1) / kWaves;
   const int grid = (int)(want < 8LL * cus ? want : 8LL * cus);
   const float c2 = scale * kLog2e;
-#define GSA_UNFOLD(D)                                                                                   \
-  hipLaunchKernelGGL((k_unfold<D>), dim3(grid), dim3(64 * kWaves), 0, st, l, (const unsigned short*)q.ptr, \
+#define GSA_UNFOLD2(D, MG)                                                                              \
+  hipLaunchKernelGGL((k_unfold<D, MG>), dim3(grid), dim3(64 * kWaves), 0, st, l, (const unsigned short*)q.ptr, \
                      q.stride_b, q.stride_t, q.stride_h, (const unsigned short*)k.ptr, k.stride_b,         \
                      k.stride_t, k.stride_h, (const unsigned short*)v.ptr, v.stride_b, v.stride_t,         \
                      v.stride_h, B, Hq, Hkv, q_begin, q_len, sel, c2, part)
+#define GSA_UNFOLD(D)                              \
+  do {                                             \
+    if (Hq / Hkv <= 4) GSA_UNFOLD2(D, 4);          \
+    else if (Hq / Hkv <= 8) GSA_UNFOLD2(D, 8);     \
+    else GSA_UNFOLD2(D, 16);                       \
+  } while (0)
   if (d == 128) GSA_UNFOLD(128);
   else if (d == 64) GSA_UNFOLD(64);
   else return fail(GSA_EUNSUPPORTED, "head dim %d (supported: 64, 128)", d);
 #undef GSA_UNFOLD
+#undef GSA_UNFOLD2
   return launch_status("gsa_attn_prefill_unfolded (unfold)");
 }
 
