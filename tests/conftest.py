@@ -7,16 +7,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # Mutation testing of the oracle (tests/test_oracle_mutations.py): a child
-# pytest process gets a planted-mistake copy of the oracle through this
-# variable and must then fail its pins.  Never set in ordinary runs.
+# pytest process gets a planted-mistake copy of one oracle module (named by
+# GSA_ORACLE_MUTANT_MODULE, default gsa_oracle) through this variable and must
+# then fail its pins.  Never set in ordinary runs.
 _MUTANT = os.environ.get("GSA_ORACLE_MUTANT")
 if _MUTANT:
-    import oracle  # noqa: E402  (the package; its module is replaced below)
-    _spec = importlib.util.spec_from_file_location("oracle.gsa_oracle", _MUTANT)
+    import oracle  # noqa: E402  (the package; the module is replaced below)
+    _name = os.environ.get("GSA_ORACLE_MUTANT_MODULE", "gsa_oracle")
+    _spec = importlib.util.spec_from_file_location("oracle." + _name, _MUTANT)
     _mod = importlib.util.module_from_spec(_spec)
-    sys.modules["oracle.gsa_oracle"] = _mod
+    sys.modules["oracle." + _name] = _mod
     _spec.loader.exec_module(_mod)
-    oracle.gsa_oracle = _mod
+    setattr(oracle, _name, _mod)
 
 
 def pytest_configure(config):

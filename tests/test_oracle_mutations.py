@@ -8,7 +8,9 @@ through would mean that part of the oracle is not pinned.
 The planted mistakes cover the layout rules (window inclusivity, sinks,
 candidacy), scoring (mean over heads and gists, head groups), selection (tie
 order, both levels, which gists score a group, which chunks are candidates),
-attention (log-sum-exp) and the block table (stream order, tile codes).
+attention (log-sum-exp) and the block table (stream order, tile codes); for
+the gzip masks, the flag threshold, the band, the literal pairs, causality,
+the ratio's divisor, the head mapping and the tile codes.
 """
 import os
 import subprocess
@@ -17,11 +19,9 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-ORACLE = os.path.join(ROOT, "oracle", "gsa_oracle.py")
-PINS = ["tests/test_oracle_pins.py", "tests/test_oracle_pins_two_level.py"]
+# module -> (its pin suites, name -> (exact text in the module, replacement))
 
-# name -> (exact text in the oracle, replacement)
-MUTANTS = {
+GSA_MUTANTS = {
     "window_inclusive": ("vis = vis | ((i - j) < max(lay.window, 1))",
                          "vis = vis | ((i - j) <= max(lay.window, 1))"),
     "no_sinks": ("vis = typ == SINK", "vis = typ == -1"),
@@ -56,17 +56,37 @@ MUTANTS = {
                           "vis = vis | ((typ == GIST) & np.isin(tm.group, group_ids))"),
 }
 
+GZIP_MUTANTS = {
+    "gz_flags_at_or_above_mean": ("return r > r.mean()", "return r >= r.mean()"),
+    "gz_band_strict": ("local = np.abs(i - j) <= w", "local = np.abs(i - j) < w"),
+    "gz_literal_either": ("lit = flags[:, None] & flags[None, :]", "lit = flags[:, None] | flags[None, :]"),
+    "gz_no_token_causality": ("return bm[blk[:, None], blk[None, :]] & (np.arange(L)[None, :] <= np.arange(L)[:, None])",
+                              "return bm[blk[:, None], blk[None, :]]"),
+    "gz_ratio_over_own_length": ("mtime=0)) / block", "mtime=0)) / len(x[i * block:(i + 1) * block])"),
+    "gz_head_map_modulo": ("h = hq // G", "h = hq % Hkv"),
+    "gz_tile_full_threshold": ("codes[qt, t] = 0 if cnt == 0 else (2 if cnt == (r1 - r0) * (c1 - c0) else 1)",
+                               "codes[qt, t] = 0 if cnt == 0 else (2 if cnt >= (r1 - r0) * (c1 - c0) - 1 else 1)"),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_planted_mistake_fails_a_pin(name, tmp_path):
-    old, new = MUTANTS[name]
-    src = open(ORACLE).read()
-    assert src.count(old) == 1, f"mutation {name}: its text is not (uniquely) in the oracle"
-    mutant = tmp_path / "gsa_oracle.py"
+SUITES = {
+    "gsa_oracle": (["tests/test_oracle_pins.py", "tests/test_oracle_pins_two_level.py"], GSA_MUTANTS),
+    "gzip_mask": (["tests/test_oracle_pins_gzip.py"], GZIP_MUTANTS),
+}
+CASES = [(mod, name) for mod, (_, muts) in SUITES.items() for name in sorted(muts)]
+
+
+@pytest.mark.parametrize("module,name", CASES, ids=[n for _, n in CASES])
+def test_planted_mistake_fails_a_pin(module, name, tmp_path):
+    pins, muts = SUITES[module]
+    old, new = muts[name]
+    src = open(os.path.join(ROOT, "oracle", module + ".py")).read()
+    assert src.count(old) == 1, f"mutation {name}: its text is not (uniquely) in oracle/{module}.py"
+    mutant = tmp_path / (module + ".py")
     mutant.write_text(src.replace(old, new))
-    env = dict(os.environ, GSA_ORACLE_MUTANT=str(mutant), PYTHONDONTWRITEBYTECODE="1")
+    env = dict(os.environ, GSA_ORACLE_MUTANT=str(mutant), GSA_ORACLE_MUTANT_MODULE=module,
+               PYTHONDONTWRITEBYTECODE="1")
     res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider",
-                          "--hypothesis-seed=0"] + PINS, cwd=ROOT, env=env, capture_output=True, text=True,
+                          "--hypothesis-seed=0"] + pins, cwd=ROOT, env=env, capture_output=True, text=True,
                          timeout=600)
     assert res.returncode == 1, (f"mutation {name} passed every pin (rc {res.returncode})\n"
                                  f"{res.stdout[-2000:]}\n{res.stderr[-2000:]}")
