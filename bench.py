@@ -404,6 +404,76 @@ def run_unfolded(w, args, torch, gsa, q, k, v):
             "kernels": "k_select_prefill; k_build_table; k_unfold + k_prefill_mfma (init from the unfold partial)"}
 
 
+def blockmask_edges(flags: np.ndarray, block: int, w: int, n_bytes: int) -> tuple:
+    """Visible (query, key) pairs of the gzip block masks of all sequences, in
+    closed form per block pair, and the causal pairs of the same lengths."""
+    nb = flags.shape[1]
+    assert n_bytes == nb * block, "whole blocks only"
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    edges = 0
+    for f in flags.astype(bool):
+        linked = ((f[:, None] & f[None, :]) | (np.abs(i - j) <= w)) & (j < i)
+        edges += int(linked.sum()) * block * block + nb * block * (block + 1) // 2
+    causal = flags.shape[0] * n_bytes * (n_bytes + 1) // 2
+    return edges, causal
+
+
+def run_blockmask(wl, args, torch, gsa):
+    """Gzip-guided block-mask prefill: host zlib flags (timed on their own),
+    then one GPU step = gsa_build_block_mask + gsa_attn_prefill_blockmask."""
+    from workloads import inputs
+    dev = torch.device("cuda:0")
+    x = inputs.mixed_bytes(wl.batch, wl.n_bytes, wl.block, seed=3)
+    t0 = time.perf_counter()
+    _, flags = gsa.gzip_block_flags(x, wl.block)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    q, k, v = inputs.random_qkv(wl.batch, wl.n_bytes, wl.hq, wl.hkv, wl.d, seed=4, dtype="bf16")
+    tq, tk, tv = (torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in (q, k, v))
+    tf = torch.from_numpy(flags).to(dev)
+    bm, bn = gsa.prefill_tile(torch.bfloat16, wl.d)
+    L = wl.n_bytes
+    nqt, nkt = -(-L // bm), -(-L // bn)
+    tables = (torch.empty((wl.batch, nqt, nkt), dtype=torch.int8, device=dev),
+              torch.empty((wl.batch, nqt), dtype=torch.int32, device=dev),
+              torch.empty((wl.batch, nqt, nkt), dtype=torch.int32, device=dev))
+    o = torch.empty((wl.batch, L, wl.hq, wl.d), dtype=torch.bfloat16, device=dev)
+    scale = 1 / math.sqrt(wl.d)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gsa.build_block_mask(tf, wl.block, wl.w, L, 0, L, bm, bn, out=tables)
+        if ev is not None:
+            ev[1].record()
+        gsa.attn_prefill_blockmask(tq, tk, tv, tables, bm, bn, 0, scale, out=(o, None))
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(5, args.steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    tab_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    att_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    edges, causal = blockmask_edges(flags, wl.block, wl.w, L)
+    alg = 4.0 * wl.d * edges * wl.hq
+    del tq, tk, tv, o
+    return {"workload": wl.name, "ms_per_step": round(wall, 4), "table_ms": round(tab_ms, 4),
+            "prefill_ms": round(att_ms, 4), "host_gzip_flags_ms": round(host_ms, 3),
+            "edges": edges, "causal_edges": causal, "edge_fraction_of_causal": round(edges / causal, 4),
+            "literal_block_fraction": round(float(flags.mean()), 4), "algorithmic_flops": alg,
+            "tflops_algorithmic_prefill": round(alg / (att_ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak_prefill": round(alg / (att_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "k_block_mask_table; k_prefill_mfma<64> (one table per sequence)"}
+
+
 def run_compact(w, args, torch, gsa, copies=2):
     """Fixed-layout decode over a compacted cache (sinks + gists + a window
     ring of raws): K/V of the whole sequence are drawn on the GPU (seeded),
@@ -486,9 +556,14 @@ def profile_pass(torch, gsa, args):
     del src, dst
     w = configs.BY_NAME[args.pass_workload]
     args.warmup, args.steps = 1, 1
-    if w.kind == "prefill":
+    if w.kind == "blockmask":
+        run_blockmask(w, args, torch, gsa)
+    elif w.kind == "prefill":
         q, k, v = inputs.prefill_inputs(w, seed=1)
-        run_prefill(w, args, torch, gsa, q, k, v)
+        if w.top_k > 0:
+            run_unfolded(w, args, torch, gsa, q, k, v)
+        else:
+            run_prefill(w, args, torch, gsa, q, k, v)
     elif w.top_k == 0:
         run_compact(w, args, torch, gsa, copies=1)
     else:
@@ -510,6 +585,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-8b", action="store_true")
     ap.add_argument("--no-unfold", action="store_true")
+    ap.add_argument("--no-blockmask", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--pass-workload", default="llama3b_gqa24x8_ratio4_k0_prefill_32k")
@@ -576,6 +652,12 @@ def main():
         log(f"prefill {wu.name}: {pu['ms_per_step']:.3f} ms/step (select {pu['select_ms']:.3f} ms, "
             f"unfold + prefill {pu['unfold_and_prefill_ms']:.3f} ms)")
         out.setdefault("prefill", []).append(pu)
+    if not args.no_blockmask:
+        wb = configs.GZIP_BLOCKMASK_PREFILL
+        pb = run_blockmask(wb, args, torch, gsa)
+        log(f"prefill {wb.name}: {pb['ms_per_step']:.3f} ms/step (table {pb['table_ms']:.3f} ms, prefill "
+            f"{pb['prefill_ms']:.3f} ms; host gzip flags {pb['host_gzip_flags_ms']:.1f} ms)")
+        out.setdefault("prefill", []).append(pb)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if not args.no_decode:

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgsa.so")
 
-GSA_OK, GSA_EINVAL, GSA_EUNSUPPORTED, GSA_EHIP = 0, 1, 2, 3
+GSA_OK, GSA_EINVAL, GSA_EUNSUPPORTED, GSA_EHIP, GSA_EHOST = 0, 1, 2, 3, 4
 GSA_F32, GSA_BF16 = 0, 1
 
 
@@ -46,7 +46,8 @@ EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_
            "gsa_decode_workspace_bytes", "gsa_decode_step", "gsa_decode_step_workspace_bytes",
            "gsa_compact_slots", "gsa_compact_gists", "gsa_compact_append", "gsa_compact_decode",
            "gsa_compact_decode_workspace_bytes", "gsa_select_prefill", "gsa_attn_prefill_unfolded",
-           "gsa_prefill_unfolded_workspace_bytes", "gsa_status_str", "gsa_last_error")
+           "gsa_prefill_unfolded_workspace_bytes", "gsa_gzip_block_flags", "gsa_build_block_mask",
+           "gsa_attn_prefill_blockmask", "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -94,6 +95,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                               I32, I32, V, V, V, V, I32, I32, F, V, ctypes.c_size_t, V]
     lib.gsa_prefill_unfolded_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.gsa_prefill_unfolded_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_gzip_block_flags.argtypes = [V, I32, I64, I32, I32, V, V]
+    lib.gsa_build_block_mask.argtypes = [V, I32, I32, I32, I32, I32, I32, I32, I32, I32, V, V, V, V]
+    lib.gsa_attn_prefill_blockmask.argtypes = [Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32, I32,
+                                               I32, V, V, V, I32, I32, F, V]
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
@@ -421,4 +426,62 @@ def attn_prefill_unfolded(layout: dict, q, k, v, sel, fixed_tables, block_m: int
                                          _bthd(o), _ptr(lse), B, Hq, Hkv, d, L, q_begin, Nq, sel.data_ptr(),
                                          table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m, block_n,
                                          float(scale), workspace.data_ptr(), workspace.numel(), _stream()))
+    return o, lse
+
+
+def gzip_block_flags(data, block: int):
+    """Ratios and literal flags of byte sequences on the host.
+
+    ``data`` is a uint8 numpy array ``[B, n_bytes]`` (or one ``bytes``).
+    Returns (ratio float32 [B, n_blocks], flags int8 [B, n_blocks])."""
+    import numpy as np
+    lib = load_library()
+    if isinstance(data, (bytes, bytearray)):
+        data = np.frombuffer(bytes(data), dtype=np.uint8)[None, :]
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    B, n = data.shape
+    nb = -(-n // block)
+    ratio = np.empty((B, nb), dtype=np.float32)
+    flags = np.empty((B, nb), dtype=np.int8)
+    _check(lib.gsa_gzip_block_flags(data.ctypes.data, B, n, n, block, ratio.ctypes.data, flags.ctypes.data))
+    return ratio, flags
+
+
+def build_block_mask(flags: torch.Tensor, block: int, w: int, seq_len: int, q_begin: int, q_len: int,
+                     block_m: int, block_n: int, out=None):
+    """Tile tables of the block mask: ``flags`` device int8 ``[B, n_blocks]``.
+    Returns (table [B, nqt, nkt], tile_cnt [B, nqt], tile_list [B, nqt, nkt])."""
+    lib = load_library()
+    assert flags.dtype == torch.int8 and flags.is_contiguous() and flags.dim() == 2
+    B, nb = flags.shape
+    nqt = -(-q_len // block_m)
+    nkt = -(-seq_len // block_n)
+    if out is None:
+        table = torch.empty((B, nqt, nkt), dtype=torch.int8, device=flags.device)
+        cnt = torch.empty((B, nqt), dtype=torch.int32, device=flags.device)
+        lst = torch.empty((B, nqt, max(nkt, 1)), dtype=torch.int32, device=flags.device)
+    else:
+        table, cnt, lst = out
+    _check(lib.gsa_build_block_mask(flags.data_ptr(), B, nb, block, w, seq_len, q_begin, q_len, block_m, block_n,
+                                    table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), _stream()))
+    return table, cnt, lst
+
+
+def attn_prefill_blockmask(q, k, v, tables, block_m: int, block_n: int, q_begin: int = 0,
+                           scale: float | None = None, out_dtype=torch.float32, want_lse: bool = True, out=None):
+    """Prefill under a block mask; ``q [B, Nq, Hq, d]``, ``k``/``v`` ``[B, L, Hkv, d]``,
+    ``tables`` from ``build_block_mask``."""
+    lib = load_library()
+    B, Nq, Hq, d = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        o = torch.empty((B, Nq, Hq, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    else:
+        o, lse = out
+    table, cnt, lst = tables
+    _check(lib.gsa_attn_prefill_blockmask(_bthd(q), _bthd(k), _bthd(v), _bthd(o), _ptr(lse), B, Hq, Hkv, d, L,
+                                          q_begin, Nq, table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m,
+                                          block_n, float(scale), _stream()))
     return o, lse

@@ -142,6 +142,7 @@ const char* gsa_status_str(gsa_status s) {
     case GSA_EINVAL: return "GSA_EINVAL";
     case GSA_EUNSUPPORTED: return "GSA_EUNSUPPORTED";
     case GSA_EHIP: return "GSA_EHIP";
+    case GSA_EHOST: return "GSA_EHOST";
   }
   return "GSA_UNKNOWN";
 }

@@ -37,7 +37,7 @@ gsa_status launch_prefill_rowwave(const Lay& l, int d, const gsa_tensor& q, cons
                                   const gsa_tensor& v, const gsa_tensor& o, float* lse, int B, int Hq,
                                   int Hkv, int q_begin, int q_len, int bm, int nqt, const int* sel,
                                   const int* selg, const int8_t* table, const int* tile_cnt,
-                                  const int* tile_list, float scale, bool fixed, hipStream_t st);
+                                  const int* tile_list, float scale, int tmode, hipStream_t st);
 
 namespace {
 
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     int64_t osb, int64_t ost, int64_t osh, float* __restrict__ lse, int Hq, int Hkv, int q_begin,
     int q_len, int nqt, const int* __restrict__ sel, const int* __restrict__ selg,
     const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
-    const int* __restrict__ tile_list, float c2, int fixed, int total, const float* __restrict__ init) {
+    const int* __restrict__ tile_list, float c2, int tmode, int total, const float* __restrict__ init) {
   using C = Cfg<D>;
   // Double-buffered K and V tiles as four separate arrays, indexed only
   // statically (the tile loop is unrolled by two): the compiler can then tell
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 
   const unsigned short* kb = k + b * ksb + h * ksh;
   const unsigned short* vb = v + b * vsb + h * vsh;
-  const int t = fixed ? 0 : b * Hkv + h;
+  const int t = tmode == 1 ? 0 : (tmode == 2 ? b : b * Hkv + h);   // table per (b, KV head) | one | per b
   const size_t trow = (size_t)t * nqt + qt;
   const int cnt = tile_cnt[trow];
   const int* list = tile_list + trow * l.nkt;
@@ -456,13 +456,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
 
 using namespace gsa;
 
-extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
-                                       gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv,
-                                       int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
-                                       const int32_t* sel, const int32_t* sel_groups,
-                                       const int8_t* table, const int32_t* tile_cnt,
-                                       const int32_t* tile_list, int32_t block_m, int32_t block_n,
-                                       float scale, void* stream) {
+namespace {
+// Table modes: 0 one table per (batch, KV head) (selections), 1 one table for
+// all (the fixed layout), 2 one table per batch entry (block masks).
+gsa_status prefill_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o,
+                          float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                          int32_t q_begin, int32_t q_len, const int32_t* sel, const int32_t* sel_groups,
+                          const int8_t* table, const int32_t* tile_cnt, const int32_t* tile_list,
+                          int32_t block_m, int32_t block_n, float scale, int tmode_in, void* stream) {
   Lay l;
   gsa_status st = make_lay(layout, seq_len, block_n, &l);
   if (st != GSA_OK) return st;
@@ -479,6 +480,7 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
     return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
   if (block_m < 1) return fail(GSA_EINVAL, "block_m %d < 1", block_m);
   const bool fixed = l.k == 0 && l.G2 == 0;
+  const int tmode = tmode_in == 2 ? 2 : (fixed ? 1 : 0);
   if (!fixed && !sel) return fail(GSA_EINVAL, "sel is required when top_k > 0");
   if (fixed && sel) return fail(GSA_EINVAL, "sel given for the fixed layout");
   if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is required with two levels");
@@ -501,7 +503,7 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr,    \
                      o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, nqt, sel,      \
-                     sel_groups, table, tile_cnt, tile_list, c2, (int)fixed, (int)total, nullptr)
+                     sel_groups, table, tile_cnt, tile_list, c2, tmode, (int)total, nullptr)
 #define GSA_MFMA(D, TO)             \
   if (lse) GSA_MFMA1(D, TO, true);  \
   else GSA_MFMA1(D, TO, false)
@@ -518,7 +520,37 @@ extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, g
   }
   if (block_n > 256) return fail(GSA_EUNSUPPORTED, "block_n %d > 256 on the row-wave path", block_n);
   return launch_prefill_rowwave(l, d, q, k, v, o, lse, B, Hq, Hkv, q_begin, q_len, block_m, nqt, sel,
-                                sel_groups, table, tile_cnt, tile_list, scale, fixed, s);
+                                sel_groups, table, tile_cnt, tile_list, scale, tmode, s);
+}
+}  // namespace
+
+extern "C" gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                       gsa_tensor o, float* lse, int32_t B, int32_t Hq, int32_t Hkv,
+                                       int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                                       const int32_t* sel, const int32_t* sel_groups,
+                                       const int8_t* table, const int32_t* tile_cnt,
+                                       const int32_t* tile_list, int32_t block_m, int32_t block_n,
+                                       float scale, void* stream) {
+  return prefill_common(layout, q, k, v, o, lse, B, Hq, Hkv, d, seq_len, q_begin, q_len, sel, sel_groups, table,
+                        tile_cnt, tile_list, block_m, block_n, scale, 0, stream);
+}
+
+extern "C" gsa_status gsa_attn_prefill_blockmask(gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o, float* lse,
+                                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                                                 int32_t q_begin, int32_t q_len, const int8_t* table,
+                                                 const int32_t* tile_cnt, const int32_t* tile_list,
+                                                 int32_t block_m, int32_t block_n, float scale, void* stream) {
+  // Every position a sink: the key stream is the physical order, and a sink
+  // is visible exactly to the queries at or after it, so PARTIAL tiles get
+  // the causal mask and the table carries the block mask.
+  if (seq_len < 1) return fail(GSA_EINVAL, "seq_len %d < 1", seq_len);
+  gsa_layout all_sinks{};
+  all_sinks.n_sink = seq_len;
+  all_sinks.chunk_len = 1;
+  all_sinks.gists_per_chunk = 1;
+  all_sinks.window = 1;
+  return prefill_common(&all_sinks, q, k, v, o, lse, B, Hq, Hkv, d, seq_len, q_begin, q_len, nullptr, nullptr,
+                        table, tile_cnt, tile_list, block_m, block_n, scale, 2, stream);
 }
 
 namespace gsa {

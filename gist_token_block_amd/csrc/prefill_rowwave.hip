@@ -46,12 +46,12 @@ __global__ __launch_bounds__(64) void k_prefill_rowwave(
     int64_t vsb, int64_t vst, int64_t vsh, TO* __restrict__ o, int64_t osb, int64_t ost,
     int64_t osh, float* __restrict__ lse, int Hq, int Hkv, int q_begin, int q_len, int bm, int nqt,
     const int* __restrict__ sel, const int* __restrict__ selg, const int8_t* __restrict__ table,
-    const int* __restrict__ tile_cnt, const int* __restrict__ tile_list, float scale, int fixed) {
+    const int* __restrict__ tile_cnt, const int* __restrict__ tile_list, float scale, int tmode) {
   const int r = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int G = Hq / Hkv, h = hq / G;
   const int i = q_begin + r;
   const int qt = r / bm;
-  const int t = fixed ? 0 : b * Hkv + h;
+  const int t = tmode == 1 ? 0 : (tmode == 2 ? b : b * Hkv + h);   // table per (b, KV head) | one | per b
   __shared__ float qs[kMaxD];
   __shared__ int ssel[64], sselg[64];
   for (int e = lane; e < d; e += 64) qs[e] = ld(q + b * qsb + r * qst + hq * qsh + e);
@@ -128,7 +128,7 @@ gsa_status launch_prefill_rowwave(const Lay& l, int d, const gsa_tensor& q, cons
                                   const gsa_tensor& v, const gsa_tensor& o, float* lse, int B, int Hq,
                                   int Hkv, int q_begin, int q_len, int bm, int nqt, const int* sel,
                                   const int* selg, const int8_t* table, const int* tile_cnt,
-                                  const int* tile_list, float scale, bool fixed, hipStream_t st) {
+                                  const int* tile_list, float scale, int tmode, hipStream_t st) {
   if (d > kMaxD) return fail(GSA_EUNSUPPORTED, "head dim %d > %d", d, kMaxD);
   dim3 grid(q_len, Hq, B);
 #define GSA_ROWWAVE(T, TO)                                                                      \
@@ -136,7 +136,7 @@ gsa_status launch_prefill_rowwave(const Lay& l, int d, const gsa_tensor& q, cons
                      q.stride_b, q.stride_t, q.stride_h, (const T*)k.ptr, k.stride_b, k.stride_t, \
                      k.stride_h, (const T*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (TO*)o.ptr, \
                      o.stride_b, o.stride_t, o.stride_h, lse, Hq, Hkv, q_begin, q_len, bm, nqt,   \
-                     sel, selg, table, tile_cnt, tile_list, scale, (int)fixed)
+                     sel, selg, table, tile_cnt, tile_list, scale, tmode)
   if (q.dtype == GSA_F32) {
     if (o.dtype == GSA_F32) GSA_ROWWAVE(float, float);
     else GSA_ROWWAVE(float, unsigned short);

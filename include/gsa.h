@@ -52,7 +52,8 @@ typedef enum {
   GSA_OK = 0,
   GSA_EINVAL = 1,        /* bad argument; nothing enqueued */
   GSA_EUNSUPPORTED = 2,  /* valid but not implemented (head dim, dtype, size) */
-  GSA_EHIP = 3           /* the HIP runtime refused a launch */
+  GSA_EHIP = 3,          /* the HIP runtime refused a launch */
+  GSA_EHOST = 4          /* a host library call (zlib) failed */
 } gsa_status;
 
 typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype;
@@ -312,6 +313,49 @@ size_t gsa_compact_decode_workspace_bytes(const gsa_layout* layout, int32_t B, i
 /* Host only.  Workspace bytes gsa_attn_decode needs for these sizes. */
 size_t gsa_decode_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
                                   int32_t d, int32_t kv_len);
+
+/* ---- Gzip-guided block masks (Gzip-guided sparse attention page, Core
+ * equations).  A sequence of bytes is cut into blocks of `block` bytes; block
+ * i's ratio is the length of its gzip encoding (zlib, level 1) over `block`,
+ * and its literal flag is 1 iff that ratio is above the mean of the
+ * sequence's ratios.  Query byte p sees key byte q iff q <= p and the blocks
+ * of p and q are linked: both flagged, or at most w blocks apart (which
+ * includes the diagonal).  Every head uses the same mask. */
+
+/* Host only: HOST pointers.  bytes [B, n_bytes] with row stride stride_b;
+ * ratio (nullable) float [B, n_blocks] and flags int8 [B, n_blocks] (out),
+ * n_blocks = ceil(n_bytes / block).  A short last block is divided by
+ * `block` too.  The flag compares integer lengths (len_i * n_blocks >
+ * sum of lengths), so it is exact.  GSA_EHOST if zlib fails. */
+gsa_status gsa_gzip_block_flags(const uint8_t* bytes, int32_t B, int64_t stride_b, int32_t n_bytes,
+                                int32_t block, float* ratio, int8_t* flags);
+
+/* Tile table of the block mask, one per sequence, key tiles in physical order
+ * (tile t = key bytes [t block_n, (t + 1) block_n), the last may be short):
+ * 0 no visible pair, 1 some (the causal diagonal), 2 all.
+ *   flags     device int8 [B, n_blocks], n_blocks = ceil(seq_len / block)
+ *   table     int8  [B, n_q_tiles, n_k_tiles] (out), n_k_tiles = ceil(seq_len / block_n)
+ *   tile_cnt  int32 [B, n_q_tiles] (out); tile_list int32 [B, n_q_tiles, n_k_tiles]
+ *             (out, ascending, row-padded as gsa_build_layout's)
+ * Requires w >= 0, block a multiple of block_m and of block_n, q_begin a
+ * multiple of block_m (a query tile then lies inside one block), else
+ * GSA_EUNSUPPORTED. */
+gsa_status gsa_build_block_mask(const int8_t* flags, int32_t B, int32_t n_blocks, int32_t block, int32_t w,
+                                int32_t seq_len, int32_t q_begin, int32_t q_len, int32_t block_m,
+                                int32_t block_n, int8_t* table, int32_t* tile_cnt, int32_t* tile_list,
+                                void* stream);
+
+/* Prefill under a block mask: softmax attention of every query row over the
+ * keys the table of gsa_build_block_mask (same block_m, block_n, q_begin,
+ * q_len) leaves visible, skipping EMPTY tiles and masking PARTIAL ones
+ * causally.  q, o [B, q_len, Hq, d]; k, v [B, seq_len, Hkv, d] (by strides);
+ * lse nullable float [B, Hq, q_len].  Tile shapes and dtypes as for
+ * gsa_attn_prefill (bf16, d in {64, 128} on MFMA with gsa_prefill_tile()). */
+gsa_status gsa_attn_prefill_blockmask(gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o, float* lse,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                                      int32_t q_begin, int32_t q_len, const int8_t* table,
+                                      const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m,
+                                      int32_t block_n, float scale, void* stream);
 
 const char* gsa_status_str(gsa_status status);
 

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import gist_token_block_amd as gsa
@@ -40,6 +41,7 @@ def test_status_strings(lib):
     assert lib.gsa_status_str(1) == b"GSA_EINVAL"
     assert lib.gsa_status_str(2) == b"GSA_EUNSUPPORTED"
     assert lib.gsa_status_str(3) == b"GSA_EHIP"
+    assert lib.gsa_status_str(4) == b"GSA_EHOST"
 
 
 def test_table_dims_stream_tiles(lib):
@@ -123,3 +125,31 @@ def test_compact_sizes(lib):
     assert gsa.compact_gists(lay, 128 + 3 * 5 + 5) == 4
     assert gsa.compact_slots(dict(n_sink=0, chunk_len=3, gists=2, window=0, top_k=0), 5) == 0 + 5 + 1
     assert gsa.compact_slots(dict(n_sink=1, chunk_len=3, gists=1, window=4, top_k=1), 5) == -1
+
+
+@pytest.mark.parametrize("n_bytes,block,seed", [(8192, 128, 0), (1000, 64, 1), (777, 100, 2), (128, 128, 3),
+                                                (300, 1, 4)])
+def test_gzip_block_flags_match_the_oracle(n_bytes, block, seed):
+    """Host-only call: ratios bit-exact (integer length / block) and flags
+    exact against the oracle on mixed synthetic bytes, ragged tails included."""
+    from oracle import gzip_mask as gm
+    from workloads import inputs
+    x = inputs.mixed_bytes(3, n_bytes, max(block, 16), seed)
+    ratio, flags = gsa.gzip_block_flags(x, block)
+    for b in range(3):
+        r = gm.block_ratios(x[b].tobytes(), block)
+        np.testing.assert_array_equal(ratio[b].astype(np.float64), r.astype(np.float32).astype(np.float64))
+        np.testing.assert_array_equal(flags[b].astype(bool), gm.literal_flags(r))
+
+
+def test_block_mask_arguments_rejected_before_launch(lib):
+    p = ctypes.c_void_p(16)
+    # block not a multiple of the tile, q_begin misaligned, wrong block count, negative band
+    assert lib.gsa_build_block_mask(p, 1, 8, 96, 1, 768, 0, 768, 128, 64, p, p, p, None) == gsa.GSA_EUNSUPPORTED
+    assert lib.gsa_build_block_mask(p, 1, 6, 128, 1, 768, 64, 704, 128, 64, p, p, p, None) == gsa.GSA_EUNSUPPORTED
+    assert lib.gsa_build_block_mask(p, 1, 5, 128, 1, 768, 0, 768, 128, 64, p, p, p, None) == gsa.GSA_EINVAL
+    assert lib.gsa_build_block_mask(p, 1, 6, 128, -1, 768, 0, 768, 128, 64, p, p, p, None) == gsa.GSA_EINVAL
+    assert lib.gsa_gzip_block_flags(None, 1, 10, 10, 4, None, p) == gsa.GSA_EINVAL
+    t16 = gsa.Tensor(16, gsa.GSA_BF16, 0, 0, 0, 0)
+    assert lib.gsa_attn_prefill_blockmask(t16, t16, t16, t16, None, 1, 1, 1, 64, 512, 0, 512, p, p, p, 64, 64,
+                                          0.1, None) == gsa.GSA_EINVAL

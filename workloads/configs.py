@@ -127,6 +127,34 @@ LLAMA3B_K16_PREFILL = Workload(
     top_k=16, n_chunks=8192,
     note="3B attention shape, 32K raw tokens, per-query top-16 unfolding")
 
+@dataclass(frozen=True)
+class BlockMaskWorkload:
+    """Prefill over byte positions under a gzip-guided block mask (Gzip-guided
+    sparse attention page, Core equations): ``block`` bytes per mask block,
+    local band of ``w`` blocks."""
+    name: str
+    dtype: str
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    n_bytes: int
+    block: int
+    w: int
+    note: str = ""
+    kind: str = "blockmask"
+
+    def as_dict(self):
+        return asdict(self)
+
+
+# 8K-byte contexts as in the page's long-context setting, the head shape of a
+# ~100M-parameter byte model (12 heads of 64), blocks of 128 bytes (one MFMA
+# query tile), a band of 2 blocks; bytes from workloads.inputs.mixed_bytes
+GZIP_BLOCKMASK_PREFILL = BlockMaskWorkload(
+    name="gzip_blockmask_prefill_b8_8k", dtype="bf16", batch=8, hq=12, hkv=12, d=64, n_bytes=8192, block=128,
+    w=2, note="8 sequences of 8192 synthetic bytes of mixed compressibility")
+
 ALL = [TINY_PREFILL_F32, LLAMA3B_K0_PREFILL, LLAMA8B_K0_PREFILL, SELECTIVE_DECODE, HIER_DECODE]
-NEXT = [COMPACT_DECODE, LLAMA3B_K16_PREFILL]
+NEXT = [COMPACT_DECODE, LLAMA3B_K16_PREFILL, GZIP_BLOCKMASK_PREFILL]
 BY_NAME = {w.name: w for w in ALL + NEXT}

@@ -17,6 +17,11 @@ Recipe (stated once, used everywhere):
     planted groups get their level-2 gist keys set that way, then planted
     chunks are drawn from inside the planted groups and get their level-1
     gist keys set that way.
+  * Byte sequences (gzip block masks): ``mixed_bytes`` -- per block a kind
+    drawn first (0.3 uniform random bytes, 0.5 pseudo-text, 0.2 a short
+    repeated pattern), then the contents block by block.  Pseudo-text is
+    words of a seeded 24-word vocabulary (2-7 lowercase letters) joined by
+    spaces, so blocks range from incompressible to highly compressible.
 """
 from __future__ import annotations
 
@@ -125,3 +130,27 @@ def decode_inputs(w, seed):
         out["plant_groups"] = gids
         out["plant_chunks"] = cids
     return out
+
+
+def mixed_bytes(batch: int, n_bytes: int, block: int, seed: int) -> np.ndarray:
+    """uint8 ``[batch, n_bytes]`` with blocks of mixed compressibility."""
+    rng = np.random.default_rng(seed)
+    nb = -(-n_bytes // block)
+    kinds = rng.choice(3, size=(batch, nb), p=[0.3, 0.5, 0.2])
+    letters = np.frombuffer(b"abcdefghijklmnopqrstuvwxyz", dtype=np.uint8)
+    vocab = [letters[rng.integers(0, 26, int(rng.integers(2, 8)))].tobytes() for _ in range(24)]
+    out = np.empty((batch, nb * block), dtype=np.uint8)
+    for b in range(batch):
+        for i in range(nb):
+            if kinds[b, i] == 0:
+                blk = rng.integers(0, 256, block, dtype=np.uint8).tobytes()
+            elif kinds[b, i] == 1:
+                words = []
+                while sum(len(w) + 1 for w in words) <= block:
+                    words.append(vocab[int(rng.integers(0, len(vocab)))])
+                blk = b" ".join(words)[:block]
+            else:
+                pat = rng.integers(0, 256, int(rng.integers(2, 9)), dtype=np.uint8).tobytes()
+                blk = (pat * (block // len(pat) + 1))[:block]
+            out[b, i * block:(i + 1) * block] = np.frombuffer(blk, dtype=np.uint8)
+    return np.ascontiguousarray(out[:, :n_bytes])
