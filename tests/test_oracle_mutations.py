@@ -10,7 +10,8 @@ candidacy), scoring (mean over heads and gists, head groups), selection (tie
 order, both levels, which gists score a group, which chunks are candidates),
 attention (log-sum-exp) and the block table (stream order, tile codes); for
 the gzip masks, the flag threshold, the band, the literal pairs, causality,
-the ratio's divisor, the head mapping and the tile codes.
+the ratio's divisor, the head mapping and the tile codes; for the backward,
+each term of the softmax derivative and the head grouping.
 """
 import os
 import subprocess
@@ -68,9 +69,19 @@ GZIP_MUTANTS = {
                                "codes[qt, t] = 0 if cnt == 0 else (2 if cnt >= (r1 - r0) * (c1 - c0) - 1 else 1)"),
 }
 
+BACKWARD_MUTANTS = {
+    "bw_no_delta": ("ds = p * (dp - delta)", "ds = p * dp"),
+    "bw_dk_unscaled": ("dk[b, idx, h, :] += scale * np.outer(ds, qr)", "dk[b, idx, h, :] += np.outer(ds, qr)"),
+    "bw_dv_from_ds": ("dv[b, idx, h, :] += np.outer(p, dor)", "dv[b, idx, h, :] += np.outer(ds, dor)"),
+    "bw_dq_from_v": ("dq[b, r, hq, :] = scale * (ds @ kk)", "dq[b, r, hq, :] = scale * (ds @ vv)"),
+    "bw_wrong_head_group": ("for hq in range(h * G, (h + 1) * G):", "for hq in range(h, h + G):"),
+    "bw_delta_from_v": ("delta = dor @ orow", "delta = dor @ vv.mean(axis=0)"),
+}
+
 SUITES = {
     "gsa_oracle": (["tests/test_oracle_pins.py", "tests/test_oracle_pins_two_level.py"], GSA_MUTANTS),
     "gzip_mask": (["tests/test_oracle_pins_gzip.py"], GZIP_MUTANTS),
+    "gsa_backward": (["tests/test_oracle_pins_backward.py"], BACKWARD_MUTANTS),
 }
 CASES = [(mod, name) for mod, (_, muts) in SUITES.items() for name in sorted(muts)]
 
