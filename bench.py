@@ -257,6 +257,53 @@ def run_prefill(w, args, torch, gsa, q, k, v):
             "tile_fill": round(alg / tile, 4)}
 
 
+def run_backward(w, args, torch, gsa, q, k, v):
+    """Prefill backward of a fixed layout: one forward (untimed) for O and
+    the log-sum-exp, then one step = gsa_attn_prefill_backward (k_bwd_dq, which
+    also forms D = rowsum(dO * O), then k_bwd_dkdv).  Algorithmic FLOPs per
+    visible (query head, key) pair: 10 d (S recomputed once, dP, dV, dK, dQ);
+    the kernels execute 14 d (S and dP are formed in both)."""
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    tdo = torch.randn(tq.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bm, bn = gsa.prefill_tile(torch.bfloat16, w.d)
+    tables = gsa.build_layout(w.layout, w.seq_len, 0, w.seq_len, bm, bn, device=dev)
+    scale = 1 / math.sqrt(w.d)
+    o, lse = gsa.attn_prefill(w.layout, tq, tk, tv, tables, bm, bn, scale=scale, out_dtype=torch.bfloat16)
+    grads = (torch.empty(tq.shape, dtype=torch.bfloat16, device=dev),
+             torch.empty(tk.shape, dtype=torch.bfloat16, device=dev),
+             torch.empty(tv.shape, dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(gsa.prefill_backward_workspace_bytes(w.batch, w.hq, w.seq_len), dtype=torch.uint8, device=dev)
+
+    def step():
+        gsa.attn_prefill_backward(w.layout, tq, tk, tv, o, tdo, lse, tables, bm, bn, scale=scale, workspace=ws,
+                                  out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(5, args.steps // 2)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    kern_ms = ev[0].elapsed_time(ev[1]) / steps
+    edges = fixed_layout_edges(w) * w.batch * w.hq
+    alg = 10.0 * w.d * edges
+    del tq, tk, tv, tdo, o, lse, grads, ws
+    return {"workload": w.name + " (backward)", "ms_per_step": round(wall, 4), "kernel_ms": round(kern_ms, 4),
+            "algorithmic_flops": alg, "executed_mfma_flops_per_pair": 14 * w.d,
+            "tflops_algorithmic": round(alg / (kern_ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(alg / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "k_bwd_dq (also D) + k_bwd_dkdv; bf16 in, bf16 grads"}
+
+
 def run_decode(w, args, torch, gsa, copies=4):
     """One decode step = the fused selection + attention (gsa_decode_step);
     caches rotate over `copies` independent buffers so the visible rows are not
@@ -586,6 +633,7 @@ def main():
     ap.add_argument("--no-8b", action="store_true")
     ap.add_argument("--no-unfold", action="store_true")
     ap.add_argument("--no-blockmask", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--pass-workload", default="llama3b_gqa24x8_ratio4_k0_prefill_32k")
@@ -652,6 +700,14 @@ def main():
         log(f"prefill {wu.name}: {pu['ms_per_step']:.3f} ms/step (select {pu['select_ms']:.3f} ms, "
             f"unfold + prefill {pu['unfold_and_prefill_ms']:.3f} ms)")
         out.setdefault("prefill", []).append(pu)
+    if not args.no_backward:
+        wbk = configs.LLAMA3B_K0_PREFILL
+        q, k, v = inputs.prefill_inputs(wbk, seed=1)
+        pbk = run_backward(wbk, args, torch, gsa, q, k, v)
+        del q, k, v
+        log(f"backward {wbk.name}: {pbk['ms_per_step']:.3f} ms/step, kernels {pbk['kernel_ms']:.3f} ms "
+            f"({pbk['tflops_algorithmic']} TFLOP/s algorithmic)")
+        out.setdefault("prefill", []).append(pbk)
     if not args.no_blockmask:
         wb = configs.GZIP_BLOCKMASK_PREFILL
         pb = run_blockmask(wb, args, torch, gsa)

@@ -47,7 +47,8 @@ EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_
            "gsa_compact_slots", "gsa_compact_gists", "gsa_compact_append", "gsa_compact_decode",
            "gsa_compact_decode_workspace_bytes", "gsa_select_prefill", "gsa_attn_prefill_unfolded",
            "gsa_prefill_unfolded_workspace_bytes", "gsa_gzip_block_flags", "gsa_build_block_mask",
-           "gsa_attn_prefill_blockmask", "gsa_status_str", "gsa_last_error")
+           "gsa_attn_prefill_blockmask", "gsa_prefill_backward_workspace_bytes", "gsa_attn_prefill_backward",
+           "gsa_attn_prefill_blockmask_backward", "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -99,6 +100,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gsa_build_block_mask.argtypes = [V, I32, I32, I32, I32, I32, I32, I32, I32, I32, V, V, V, V]
     lib.gsa_attn_prefill_blockmask.argtypes = [Tensor, Tensor, Tensor, Tensor, V, I32, I32, I32, I32, I32, I32,
                                                I32, V, V, V, I32, I32, F, V]
+    lib.gsa_prefill_backward_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.gsa_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_attn_prefill_backward.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor, Tensor, Tensor,
+                                              I32, I32, I32, I32, I32, I32, I32, V, V, V, I32, I32, F, V,
+                                              ctypes.c_size_t, V]
+    lib.gsa_attn_prefill_blockmask_backward.argtypes = [Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor, Tensor,
+                                                        Tensor, I32, I32, I32, I32, I32, I32, I32, V, V, V, I32, I32,
+                                                        F, V, ctypes.c_size_t, V]
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
@@ -107,7 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         if name not in ("gsa_score_columns", "gsa_decode_workspace_bytes", "gsa_status_str",
                         "gsa_last_error", "gsa_decode_step_workspace_bytes", "gsa_compact_slots",
                         "gsa_compact_gists", "gsa_compact_decode_workspace_bytes",
-                        "gsa_prefill_unfolded_workspace_bytes"):
+                        "gsa_prefill_unfolded_workspace_bytes", "gsa_prefill_backward_workspace_bytes"):
             getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -485,3 +494,39 @@ def attn_prefill_blockmask(q, k, v, tables, block_m: int, block_n: int, q_begin:
                                           q_begin, Nq, table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m,
                                           block_n, float(scale), _stream()))
     return o, lse
+
+
+def prefill_backward_workspace_bytes(B: int, Hq: int, q_len: int) -> int:
+    return int(load_library().gsa_prefill_backward_workspace_bytes(B, Hq, q_len))
+
+
+def attn_prefill_backward(layout, q, k, v, o, do, lse, tables, block_m: int, block_n: int, q_begin: int = 0,
+                          scale: float | None = None, grad_dtype=torch.float32, workspace=None, out=None):
+    """dq, dk, dv of the block-sparse prefill.  ``layout`` is a layout dict
+    (fixed layout) or the string "blockmask" (tables of build_block_mask).
+    ``q``/``do``/``o`` ``[B, Nq, Hq, d]``, ``k``/``v`` ``[B, L, Hkv, d]``,
+    ``lse [B, Hq, Nq]`` from the forward."""
+    lib = load_library()
+    B, Nq, Hq, d = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(max(prefill_backward_workspace_bytes(B, Hq, Nq), 256), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        dq = torch.empty((B, Nq, Hq, d), dtype=grad_dtype, device=q.device)
+        dk = torch.empty((B, L, Hkv, d), dtype=grad_dtype, device=q.device)
+        dv = torch.empty((B, L, Hkv, d), dtype=grad_dtype, device=q.device)
+    else:
+        dq, dk, dv = out
+    assert lse.dtype == torch.float32 and lse.is_contiguous()
+    table, cnt, lst = tables
+    common = (_bthd(q), _bthd(k), _bthd(v), _bthd(o), _bthd(do), lse.data_ptr(), _bthd(dq), _bthd(dk), _bthd(dv),
+              B, Hq, Hkv, d, L, q_begin, Nq, table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m, block_n,
+              float(scale), workspace.data_ptr(), workspace.numel(), _stream())
+    if isinstance(layout, str):
+        assert layout == "blockmask"
+        _check(lib.gsa_attn_prefill_blockmask_backward(*common))
+    else:
+        _check(lib.gsa_attn_prefill_backward(ctypes.byref(make_layout(layout)), *common))
+    return dq, dk, dv

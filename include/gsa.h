@@ -357,6 +357,40 @@ gsa_status gsa_attn_prefill_blockmask(gsa_tensor q, gsa_tensor k, gsa_tensor v, 
                                       const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m,
                                       int32_t block_n, float scale, void* stream);
 
+/* ---- Backward of the block-sparse prefill (Forget, Then Recall ... Gist
+ * Sparse Attention, abstract: the sparse pattern is trained end to end; the
+ * UniGist summary measures forward and backward latency, Experimental setup).
+ * With s = scale q.k, P the softmax over each row's visible keys and
+ * D = rowsum(dO * O):  dS = P (dO V^T - D), dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO, keys summed over the query heads of their KV group.  P is
+ * recomputed from the forward's log-sum-exp.
+ *   q, do, o, dq  [B, q_len, Hq, d] (by strides); k, v, dk, dv [B, seq_len, Hkv, d]
+ *   q, k, v, do   bf16; o F32 or bf16 (the forward's output); dq, dk, dv F32
+ *                 or bf16 (all three alike)
+ *   lse           float [B, Hq, q_len], natural log, from the forward
+ *   table, tile_cnt, tile_list  the forward's tables (gsa_prefill_tile() shape)
+ *   ws            gsa_prefill_backward_workspace_bytes() bytes (D is kept there)
+ * Every key position of dk and dv is written (zero where no query row sees it).
+ * Requires d in {64, 128}.  Layouts: the fixed layout (top_k = 0, one level);
+ * other layouts return GSA_EUNSUPPORTED. */
+size_t gsa_prefill_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t q_len);
+gsa_status gsa_attn_prefill_backward(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                     gsa_tensor o, gsa_tensor dO, const float* lse, gsa_tensor dq, gsa_tensor dk,
+                                     gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
+                                     int32_t q_begin, int32_t q_len, const int8_t* table, const int32_t* tile_cnt,
+                                     const int32_t* tile_list, int32_t block_m, int32_t block_n, float scale,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* The same backward under a gzip-guided block mask: tables from
+ * gsa_build_block_mask (Gzip-guided sparse attention page, Core equations). */
+gsa_status gsa_attn_prefill_blockmask_backward(gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o,
+                                               gsa_tensor dO, const float* lse, gsa_tensor dq, gsa_tensor dk,
+                                               gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                                               int32_t seq_len, int32_t q_begin, int32_t q_len, const int8_t* table,
+                                               const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m,
+                                               int32_t block_n, float scale, void* ws, size_t ws_bytes,
+                                               void* stream);
+
 const char* gsa_status_str(gsa_status status);
 
 /* Message of the last non-OK return on the calling thread ("" if none). */
