@@ -603,7 +603,10 @@ def profile_pass(torch, gsa, args):
     del src, dst
     w = configs.BY_NAME[args.pass_workload]
     args.warmup, args.steps = 1, 1
-    if w.kind == "blockmask":
+    if args.pass_backward:
+        q, k, v = inputs.prefill_inputs(w, seed=1)
+        run_backward(w, args, torch, gsa, q, k, v)
+    elif w.kind == "blockmask":
         run_blockmask(w, args, torch, gsa)
     elif w.kind == "prefill":
         q, k, v = inputs.prefill_inputs(w, seed=1)
@@ -637,6 +640,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--pass-workload", default="llama3b_gqa24x8_ratio4_k0_prefill_32k")
+    ap.add_argument("--pass-backward", action="store_true", help="profile pass: the backward of the workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "

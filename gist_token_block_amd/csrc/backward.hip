@@ -99,7 +99,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     const unsigned short* __restrict__ v, int64_t vsb, int64_t vst, int64_t vsh,
     const void* __restrict__ o, int64_t osb, int64_t ost, int64_t osh,
     const unsigned short* __restrict__ dO, int64_t dsb, int64_t dst, int64_t dsh, const float* __restrict__ lse,
-    TO* __restrict__ dq, int64_t gsb, int64_t gst, int64_t gsh, float* __restrict__ delta, int Hq, int Hkv,
+    TO* __restrict__ dq, int64_t gsb, int64_t gst, int64_t gsh, float* __restrict__ delta,
+    float* __restrict__ lse2_out, int Hq, int Hkv,
     int q_begin, int q_len, int nqt, const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
     const int* __restrict__ tile_list, float c2, float scale, int tmode, int total) {
   using C = BCfg<D>;
@@ -177,7 +178,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
   }
   const float Dlt = dsum + __shfl_xor(dsum, 32);
   const float lse2 = rvalid ? lse[((size_t)b * Hq + hq) * q_len + rr] * kLog2e : 0.f;
-  if (rvalid && h2 == 0) delta[((size_t)b * Hq + hq) * q_len + r] = Dlt;
+  if (rvalid && h2 == 0) {
+    delta[((size_t)b * Hq + hq) * q_len + r] = Dlt;
+    lse2_out[((size_t)b * Hq + hq) * q_len + r] = lse2;
+  }
   if (h2 == 0) {
     const int row = wave * 32 + n;
 #pragma unroll
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
     const unsigned short* __restrict__ v, int64_t vsb, int64_t vst, int64_t vsh,
-    const unsigned short* __restrict__ dO, int64_t dsb, int64_t dst, int64_t dsh, const float* __restrict__ lse,
+    const unsigned short* __restrict__ dO, int64_t dsb, int64_t dst, int64_t dsh, const float* __restrict__ lse2,
     const float* __restrict__ delta, TO* __restrict__ dk, int64_t ksb_o, int64_t kst_o, int64_t ksh_o,
     TO* __restrict__ dv, int64_t vsb_o, int64_t vst_o, int64_t vsh_o, int Hq, int Hkv, int q_begin, int q_len,
     int nqt, const int8_t* __restrict__ table, float c2, float scale, int tmode) {
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
   constexpr int NBUF = 3;
   // Q and dO of a 64-row stage, three deep (two prefetches in flight)
   __shared__ __attribute__((aligned(1024))) unsigned short SB[NBUF * 2 * kStage * D];
-  __shared__ __attribute__((aligned(16))) float LB[NBUF][kStage], EB[NBUF][kStage];   // lse, D
+  __shared__ __attribute__((aligned(16))) float LB[NBUF][kStage], EB[NBUF][kStage];   // lse log2 e, D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h2 = lane >> 5;
@@ -414,9 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     const int rr = imin(r0 + lane, q_len - 1);
     const size_t ri = ((size_t)b * Hq + hq) * q_len + rr;
     if (wv == 1) __builtin_amdgcn_global_load_lds((glb_void_ptr)(delta + ri), (lds_void_ptr)&EB[bi][0], 4, 0, 0);
-    else if (wv == 0) __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
-    else {   // waves 2, 3: the same lse again, keeping the per-wave count equal
-      __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
+    else if (wv == 0) __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse2 + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
+    else {   // waves 2, 3: the same row again, keeping the per-wave count equal
+      __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse2 + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
     }
   };
 
@@ -511,9 +515,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     a_cd = b_cd;
     b_r0 = c_r0;
     b_cd = c_cd;
-    if (code == 0 || !tile_ok) continue;   // this wave's tile sees none of these rows
+    // Every wave computes every stage (a wave whose tile has code 0 here masks
+    // everything): no divergent path around the accumulators.
     const unsigned short* Qb = SB + bi * 2 * kStage * D;
     const unsigned short* Ob = Qb + kStage * D;
+    const bool needmask = code != 2 || width < kBN || r0 + kStage > q_len || !tile_ok;   // wave-uniform
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // S = Q K^T and dP = dO V^T for rows 32 qb + (slots), this lane's key
@@ -526,38 +532,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dp, 0, 0, 0);
       }
       // slot j is stage row 32 qb + 8 (j / 4) + 4 h2 + j % 4
-      f32x4 lsev[4], dlv[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        lsev[jj] = *reinterpret_cast<const f32x4*>(&LB[bi][32 * qb + 8 * jj + 4 * h2]);
-        dlv[jj] = *reinterpret_cast<const f32x4*>(&EB[bi][32 * qb + 8 * jj + 4 * h2]);
-      }
-      unsigned vis = kvalid ? 0xffffu : 0u;
-      if (code != 2 || width < kBN || r0 + kStage > q_len) {
-        unsigned m = 0;
+      if (needmask) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int rr = r0 + 32 * qb + 8 * (j >> 2) + 4 * h2 + (j & 3);
-          bool ok = false;
-          if (rr < q_len) {
+          bool ok = code != 0 && kvalid && rr < q_len;
+          if (ok) {
             int lo, hi;
             stream_range(l, kind, q_begin + rr, lo, hi);
             const int u = u0 + key;
             ok = u >= lo && u < hi;
           }
-          m |= (unsigned)ok << j;
+          if (!ok) s[j] = -__builtin_inff();
         }
-        vis &= m;
       }
-      // P = exp2(s c2 - lse log2 e), dS = P (dP - D)
-      f32x16 pm, dsm;
+      // P = exp2(s c2 - lse log2 e), dS = P (dP - D), in place
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float l2 = lsev[j >> 2][j & 3] * kLog2e;
-        const float pr = ((vis >> j) & 1u) ? __builtin_amdgcn_exp2f(fmaf(s[j], c2, -l2)) : 0.f;
-        pm[j] = pr;
-        dsm[j] = pr * (dp[j] - dlv[j >> 2][j & 3]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&LB[bi][32 * qb + 8 * jj + 4 * h2]);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&EB[bi][32 * qb + 8 * jj + 4 * h2]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * jj + e;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -l2[e]));
+          s[j] = pr;
+          dp[j] = pr * (dp[j] - dl[e]);
+        }
       }
+      f32x16& pm = s;
+      f32x16& dsm = dp;
       // dV += P^T dO, dK += dS^T Q (A: slots 8 xx .. + 7 = rows 16 xx + 8 (e / 4)
       // + 4 h2 + e % 4 of block qb; B: dO, Q read transposed at those rows)
 #pragma unroll
@@ -627,14 +630,15 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
   if (block_m != kBM || block_n != kBN)
     return fail(GSA_EINVAL, "the backward needs the %dx%d table (got %dx%d)", kBM, kBN, block_m, block_n);
   if (!lse || !table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "lse or table pointers are NULL");
-  const size_t need = (size_t)B * Hq * q_len * sizeof(float);
+  const size_t need = 2 * (size_t)B * Hq * q_len * sizeof(float);
   if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes < %zu", ws_bytes, need);
   const int nqt = (q_len + kBM - 1) / kBM;
   const long long total = (long long)B * Hkv * nqt * (Hq / Hkv);
   if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
   hipStream_t s = (hipStream_t)stream;
   const float c2 = scale * kLog2e;
-  float* delta = (float*)ws;
+  float* delta = (float*)ws;                              // D = rowsum(dO O)
+  float* lse2 = delta + (size_t)B * Hq * q_len;            // lse log2 e
   const bool of32 = o.dtype == GSA_F32;
 #define GSA_DQ(D, TO, OF)                                                                                        \
   hipLaunchKernelGGL((k_bwd_dq<D, TO, OF>), dim3((unsigned)total), dim3(kThreads), 0, s, l,                      \
@@ -642,7 +646,7 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                            \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (const void*)o.ptr,        \
                      o.stride_b, o.stride_t, o.stride_h, (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, \
-                     dO.stride_h, lse, (TO*)dq.ptr, dq.stride_b, dq.stride_t, dq.stride_h, delta, Hq, Hkv,         \
+                     dO.stride_h, lse, (TO*)dq.ptr, dq.stride_b, dq.stride_t, dq.stride_h, delta, lse2, Hq, Hkv,   \
                      q_begin, q_len, nqt, table, tile_cnt, tile_list, c2, scale, tmode, (int)total)
 #define GSA_KV(D, TO)                                                                                              \
   hipLaunchKernelGGL((k_bwd_dkdv<D, TO>), dim3((unsigned)((l.nkt + 1) / 2), (unsigned)Hkv, (unsigned)B),        \
@@ -650,7 +654,7 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      l, (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                           \
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                              \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h,                              \
-                     (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, dO.stride_h, lse, delta, (TO*)dk.ptr, \
+                     (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, dO.stride_h, lse2, delta, (TO*)dk.ptr, \
                      dk.stride_b, dk.stride_t, dk.stride_h, (TO*)dv.ptr, dv.stride_b, dv.stride_t, dv.stride_h, Hq, \
                      Hkv, q_begin, q_len, nqt, table, c2, scale, tmode)
 #define GSA_BW(D, TO)                      \
@@ -677,7 +681,7 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
 
 extern "C" size_t gsa_prefill_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t q_len) {
   if (B < 1 || Hq < 1 || q_len < 0) return 0;
-  return (size_t)B * Hq * q_len * sizeof(float);
+  return 2 * (size_t)B * Hq * q_len * sizeof(float);
 }
 
 extern "C" gsa_status gsa_attn_prefill_backward(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,

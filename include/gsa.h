@@ -369,7 +369,8 @@ gsa_status gsa_attn_prefill_blockmask(gsa_tensor q, gsa_tensor k, gsa_tensor v, 
  *                 or bf16 (all three alike)
  *   lse           float [B, Hq, q_len], natural log, from the forward
  *   table, tile_cnt, tile_list  the forward's tables (gsa_prefill_tile() shape)
- *   ws            gsa_prefill_backward_workspace_bytes() bytes (D is kept there)
+ *   ws            gsa_prefill_backward_workspace_bytes() bytes (D and the base-2
+ *                 log-sum-exp per row are kept there between the two kernels)
  * Every key position of dk and dv is written (zero where no query row sees it).
  * Requires d in {64, 128}.  Layouts: the fixed layout (top_k = 0, one level);
  * other layouts return GSA_EUNSUPPORTED. */
