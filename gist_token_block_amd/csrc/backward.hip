@@ -15,9 +15,11 @@
 // sits in LDS in the transposed-read swizzle and V in the row-read one.  The
 // kernel also writes D for the second kernel.
 //
-// k_bwd_dkdv: one workgroup per (batch, KV head, two key tiles); each wave
-// owns 32 keys of one tile, holds their K and V rows as MFMA operands in
-// registers, and accumulates their dK and dV over every row of every stage.
+// k_bwd_dkdv: one workgroup of 8 waves per (batch, KV head, two key tiles);
+// each wave owns 16 keys of one tile, holds their K and V rows as MFMA
+// operands in registers (v_mfma_f32_16x16x32_bf16, so a wave needs about half
+// the registers of a 32-key form and two waves fit a SIMD), and accumulates
+// their dK and dV over every row of every stage.
 // The stages are the query tiles whose table code for either key tile is
 // non-zero, for every query head of the KV group, each cut in two 64-row
 // halves; Q, dO, log-sum-exp and D of a stage go through LDS three deep, so
@@ -341,8 +343,22 @@ template <int N> __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// v_mfma_f32_16x16x32_bf16 operands: A [m = lane % 16][k = 8 (lane / 16) + e],
+// B [k = 8 (lane / 16) + e][n = lane % 16], C [m = 4 (lane / 16) + j][n = lane % 16].
+constexpr int kWaves16 = 8;
+
+// Transposed-read B operand of the 16x16x32 products: 8 bf16 of column
+// d = lane % 16 + 16 mt over the rows base + (e < 4 ? 4 g + e : 16 + 4 g + e - 4),
+// g = lane / 16, of a [rows][D] tile stored in the swz_tr swizzle.
+template <int D> __device__ inline bf16x8 tr_pair16(const unsigned short* base, int tr_off, int row0) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + tr_off + row0 * D));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + tr_off + (row0 + 16) * D));
+  const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wh[0], wh[1]});
+}
+
 template <int D, typename TO>
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
+__global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
     const unsigned short* __restrict__ v, int64_t vsb, int64_t vst, int64_t vsh,
@@ -350,55 +366,59 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     const float* __restrict__ delta, TO* __restrict__ dk, int64_t ksb_o, int64_t kst_o, int64_t ksh_o,
     TO* __restrict__ dv, int64_t vsb_o, int64_t vst_o, int64_t vsh_o, int Hq, int Hkv, int q_begin, int q_len,
     int nqt, const int8_t* __restrict__ table, float c2, float scale, int tmode) {
-  using C = BCfg<D>;
+  constexpr int PPR = D / 8, RPI = 64 / PPR;
+  constexpr int NIW = kStage / RPI / kWaves16;   // wave loads per tensor per stage
+  constexpr int KS = D / 32;                     // k-steps of S and dP
+  constexpr int MT = D / 16;                     // 16-wide d tiles of dK and dV
   constexpr int NBUF = 3;
+  static_assert(NIW >= 1, "stage rows per wave");
   // Q and dO of a 64-row stage, three deep (two prefetches in flight)
   __shared__ __attribute__((aligned(1024))) unsigned short SB[NBUF * 2 * kStage * D];
   __shared__ __attribute__((aligned(16))) float LB[NBUF][kStage], EB[NBUF][kStage];   // lse log2 e, D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, h2 = lane >> 5;
+  const int col = lane & 15, grp = lane >> 4;
   const int h = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  // key tiles 2 x and 2 x + 1; wave w takes keys [32 (w & 1), + 32) of tile 2 x + (w >> 1)
+  // key tiles 2 x and 2 x + 1; wave w takes keys [16 (w & 3), + 16) of tile 2 x + (w >> 2)
   const int kt0 = 2 * blockIdx.x;
-  const int ktw = kt0 + (wave >> 1);
+  const int ktw = kt0 + (wave >> 2);
   const bool tile_ok = ktw < l.nkt;
   int kind = 0, u0 = 0, u1 = 0, slot = 0;
   if (tile_ok) slot = tile_span(l, ktw, kind, u0, u1);
   const int width = u1 - u0;
   const StreamMap sm = slot_map(l, slot);
-  const int key = 32 * (wave & 1) + n;
+  const int key = 16 * (wave & 3) + col;   // this lane's key (N of S and dP)
   const bool kvalid = tile_ok && key < width;
   const int p_key = kvalid ? map_pos(sm, u0 + key) : 0;
 
-  // K^T and V^T operands (B of S = Q K^T, dP = dO V^T): d = 8 h2 + 16 ks + 0..7
-  bf16x8 kreg[C::KS], vreg[C::KS];
+  // K^T and V^T operands (B of S = Q K^T, dP = dO V^T): d = 32 ks + 8 g + 0..7
+  bf16x8 kreg[KS], vreg[KS];
   {
     const unsigned short* krow = k + b * ksb + (int64_t)p_key * kst + h * ksh;
     const unsigned short* vrow = v + b * vsb + (int64_t)p_key * vst + h * vsh;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 8 * h2 + 16 * ks));
-      vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow + 8 * h2 + 16 * ks));
+    for (int ks = 0; ks < KS; ++ks) {
+      kreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32 * ks + 8 * grp));
+      vreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow + 32 * ks + 8 * grp));
     }
   }
-  f32x16 dkacc[C::MT], dvacc[C::MT];
+  f32x4 dkacc[MT], dvacc[MT];
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) {
-    dkacc[mt] = f32x16{};
-    dvacc[mt] = f32x16{};
+  for (int mt = 0; mt < MT; ++mt) {
+    dkacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dvacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int t = tmode == 1 ? 0 : (tmode == 2 ? b : b * Hkv + h);
   const int8_t* col0 = table + (size_t)t * nqt * l.nkt + kt0;   // codes of tile kt0 (stride nkt)
   const bool has1 = kt0 + 1 < l.nkt;
 
-  const int srow = lane / C::PPR, sslot = lane % C::PPR;
+  const int srow = lane / PPR, sslot = lane % PPR;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  int soff[C::NIW];
+  int soff[NIW];
 #pragma unroll
-  for (int it = 0; it < C::NIW; ++it) soff[it] = 8 * (sslot ^ swz_tr<D>((wave * C::NIW + it) * C::RPI + srow));
+  for (int it = 0; it < NIW; ++it) soff[it] = 8 * (sslot ^ swz_tr<D>((wave * NIW + it) * RPI + srow));
   // every wave issues exactly NIW * 2 + 1 vector loads per stage (one of them
   // lse or D, or a dummy re-load of lse)
   auto fetch = [&](int r0, int hq, int bi) __attribute__((always_inline)) {
@@ -407,9 +427,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     const unsigned short* qb = q + b * qsb + hq * qsh;
     const unsigned short* ob = dO + b * dsb + hq * dsh;
 #pragma unroll
-    for (int it = 0; it < C::NIW; ++it) {
-      const int wi = wv * C::NIW + it;
-      const int rr = imin(r0 + wi * C::RPI + srow, q_len - 1);
+    for (int it = 0; it < NIW; ++it) {
+      const int wi = wv * NIW + it;
+      const int rr = imin(r0 + wi * RPI + srow, q_len - 1);
       __builtin_amdgcn_global_load_lds((glb_void_ptr)(qb + (int64_t)rr * qst + soff[it]),
                                        (lds_void_ptr)(Qd + wi * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((glb_void_ptr)(ob + (int64_t)rr * dst + soff[it]),
@@ -418,31 +438,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     const int rr = imin(r0 + lane, q_len - 1);
     const size_t ri = ((size_t)b * Hq + hq) * q_len + rr;
     if (wv == 1) __builtin_amdgcn_global_load_lds((glb_void_ptr)(delta + ri), (lds_void_ptr)&EB[bi][0], 4, 0, 0);
-    else if (wv == 0) __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse2 + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
-    else {   // waves 2, 3: the same row again, keeping the per-wave count equal
-      __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse2 + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
-    }
+    else __builtin_amdgcn_global_load_lds((glb_void_ptr)(lse2 + ri), (lds_void_ptr)&LB[bi][0], 4, 0, 0);
   };
 
-  const int tg = lane >> 4, tj = lane & 15;
-  const int tr_row = 4 * (tg >> 1) + (tj >> 2);
-  const int tr_piece = 2 * (tg & 1) + ((tj & 3) >> 1);
-  const int tr_half = tj & 1;
-  int tr_off[C::MT];
+  // A-operand row reads (rows 16 t + col, d = 32 ks + 8 g + 0..7; rows 16 t + r
+  // share the swizzle of r) and transposed-read offsets (rows 4 g + col / 4)
+  int ar_off[KS], tr_off[MT];
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) {
-    tr_off[mt] = tr_row * D + 8 * ((4 * mt + tr_piece) ^ swz_tr<D>(tr_row)) + 4 * tr_half;
-    asm volatile("" : "+v"(tr_off[mt]));
+  for (int ks = 0; ks < KS; ++ks) {
+    ar_off[ks] = col * D + 8 * ((grp + 4 * ks) ^ swz_tr<D>(col));
+    asm volatile("" : "+v"(ar_off[ks]));
   }
-  int ar_off[2][C::KS];   // A-operand rows 32 qb + n
+  {
+    const int trow = 4 * grp + (col >> 2);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int arow = 32 * qb + n;
-      ar_off[qb][ks] = arow * D + 8 * ((h2 + 2 * ks) ^ swz_tr<D>(arow));
-      asm volatile("" : "+v"(ar_off[qb][ks]));
+    for (int mt = 0; mt < MT; ++mt) {
+      tr_off[mt] = trow * D + 8 * ((2 * mt + ((col & 3) >> 1)) ^ swz_tr<D>(trow)) + 4 * (col & 1);
+      asm volatile("" : "+v"(tr_off[mt]));
     }
+  }
 
   // The stage sequence: query tiles where either tile's code is non-zero,
   // ascending (scanned 64 at a time by ballot; the codes stay in lanes), then
@@ -478,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     }
     return find_tile();
   };
+
   // Stage e uses buffer e % 3.  A is the stage being computed, B and C the
   // (up to) two in flight behind it: first row and this wave's code.
   int a_r0 = 0, a_cd = 0, b_r0 = 0, b_cd = 0, c_r0 = 0, c_cd = 0;
@@ -485,14 +500,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
   bool more = next_stage();
   if (more) {
     a_r0 = s_qt * kBM + kStage * s_half;
-    a_cd = (wave >> 1) ? s_c1 : s_c0;
+    a_cd = (wave >> 2) ? s_c1 : s_c0;
     fetch(a_r0, h * G + s_gq, 0);
     nst = 1;
     more = next_stage();
   }
   if (more) {
     b_r0 = s_qt * kBM + kStage * s_half;
-    b_cd = (wave >> 1) ? s_c1 : s_c0;
+    b_cd = (wave >> 2) ? s_c1 : s_c0;
     fetch(b_r0, h * G + s_gq, 1);
     nst = 2;
     more = next_stage();
@@ -500,12 +515,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
   for (int cur = 0; cur < nst; ++cur) {
     const int bi = cur % NBUF;
     // this stage's loads are older than the (at most one) later stage's
-    if (cur + 1 < nst) wait_vmcnt<C::NIW * 2 + 1>();
+    if (cur + 1 < nst) wait_vmcnt<NIW * 2 + 1>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (more) {   // refill the buffer freed by stage cur - 1
       c_r0 = s_qt * kBM + kStage * s_half;
-      c_cd = (wave >> 1) ? s_c1 : s_c0;
+      c_cd = (wave >> 2) ? s_c1 : s_c0;
       fetch(c_r0, h * G + s_gq, nst % NBUF);
       ++nst;
       more = next_stage();
@@ -521,21 +536,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
     const unsigned short* Ob = Qb + kStage * D;
     const bool needmask = code != 2 || width < kBN || r0 + kStage > q_len || !tile_ok;   // wave-uniform
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T for rows 32 qb + (slots), this lane's key
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qp = 0; qp < 2; ++qp) {   // 32-row blocks of the stage
+      // S = Q K^T and dP = dO V^T for the 16-row blocks 2 qp + tt: lane holds
+      // rows 32 qp + 16 tt + 4 g + j, this lane's key
+      f32x4 s[2], dp[2];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qb + ar_off[qb][ks]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ob + ar_off[qb][ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ks], dp, 0, 0, 0);
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int rb = (32 * qp + 16 * tt) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qb + rb + ar_off[ks]);
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Ob + rb + ar_off[ks]);
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kreg[ks], s[tt], 0, 0, 0);
+          dp[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vreg[ks], dp[tt], 0, 0, 0);
+        }
       }
-      // slot j is stage row 32 qb + 8 (j / 4) + 4 h2 + j % 4
       if (needmask) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rr = r0 + 32 * qb + 8 * (j >> 2) + 4 * h2 + (j & 3);
+        // visibility bits first (bit 4 tt + j), then a select with static
+        // indices: no dynamically indexed register write under divergence
+        unsigned m = 0;
+        for (int x = 0; x < 8; ++x) {
+          const int rr = r0 + 32 * qp + 16 * (x >> 2) + 4 * grp + (x & 3);
           bool ok = code != 0 && kvalid && rr < q_len;
           if (ok) {
             int lo, hi;
@@ -543,53 +566,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_dkdv(
             const int u = u0 + key;
             ok = u >= lo && u < hi;
           }
-          if (!ok) s[j] = -__builtin_inff();
+          m |= (unsigned)ok << x;
         }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[tt][j] = ((m >> (4 * tt + j)) & 1u) ? s[tt][j] : kNegBig;
       }
-      // P = exp2(s c2 - lse log2 e), dS = P (dP - D), in place
+      // P = exp2(s c2 - lse log2 e), dS = P (dP - D); packed as A operands,
+      // element e <-> row 32 qp + (e < 4 ? 4 g + e : 16 + 4 g + e - 4)
+      unsigned wp[4], wd[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&LB[bi][32 * qb + 8 * jj + 4 * h2]);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(&EB[bi][32 * qb + 8 * jj + 4 * h2]);
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&LB[bi][32 * qp + 16 * tt + 4 * grp]);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&EB[bi][32 * qp + 16 * tt + 4 * grp]);
+        float pr[4], ds[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * jj + e;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -l2[e]));
-          s[j] = pr;
-          dp[j] = pr * (dp[j] - dl[e]);
+        for (int j = 0; j < 4; ++j) {
+          pr[j] = __builtin_amdgcn_exp2f(fmaf(s[tt][j], c2, -l2[j]));
+          ds[j] = pr[j] * (dp[tt][j] - dl[j]);
         }
+        wp[2 * tt] = pack_bf16x2(pr[0], pr[1]);
+        wp[2 * tt + 1] = pack_bf16x2(pr[2], pr[3]);
+        wd[2 * tt] = pack_bf16x2(ds[0], ds[1]);
+        wd[2 * tt + 1] = pack_bf16x2(ds[2], ds[3]);
       }
-      f32x16& pm = s;
-      f32x16& dsm = dp;
-      // dV += P^T dO, dK += dS^T Q (A: slots 8 xx .. + 7 = rows 16 xx + 8 (e / 4)
-      // + 4 h2 + e % 4 of block qb; B: dO, Q read transposed at those rows)
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{wp[0], wp[1], wp[2], wp[3]});
+      const bf16x8 da = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
+      // dV += P^T dO, dK += dS^T Q over the 16-wide d tiles
 #pragma unroll
-      for (int xx = 0; xx < 2; ++xx) {
-        const bf16x8 pa = pack8(pm, xx), da = pack8(dsm, xx);
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          dvacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand<D>(Ob, tr_off[mt], 2 * qb + xx),
-                                                              dvacc[mt], 0, 0, 0);
-          dkacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand<D>(Qb, tr_off[mt], 2 * qb + xx),
-                                                              dkacc[mt], 0, 0, 0);
-        }
+      for (int mt = 0; mt < MT; ++mt) {
+        dvacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, tr_pair16<D>(Ob, tr_off[mt], 32 * qp), dvacc[mt], 0, 0,
+                                                            0);
+        dkacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, tr_pair16<D>(Qb, tr_off[mt], 32 * qp), dkacc[mt], 0, 0,
+                                                            0);
       }
     }
   }
 
-  // lane holds dK[key 8 (j / 4) + 4 h2 + j % 4 of its 32][d = 32 mt + n]
+  // lane holds dK[key 16 (w & 3) + 4 g + j][d = 16 mt + col]
   if (tile_ok) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = 32 * (wave & 1) + 8 * (j >> 2) + 4 * h2 + (j & 3);
+    for (int j = 0; j < 4; ++j) {
+      const int kk = 16 * (wave & 3) + 4 * grp + j;
       if (kk < width) {
         const int p = map_pos(sm, u0 + kk);
         TO* krow = dk + b * ksb_o + (int64_t)p * kst_o + h * ksh_o;
         TO* vrow = dv + b * vsb_o + (int64_t)p * vst_o + h * vsh_o;
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          put1<TO>(krow + 32 * mt + n, dkacc[mt][j] * scale);
-          put1<TO>(vrow + 32 * mt + n, dvacc[mt][j]);
+        for (int mt = 0; mt < MT; ++mt) {
+          put1<TO>(krow + 16 * mt + col, dkacc[mt][j] * scale);
+          put1<TO>(vrow + 16 * mt + col, dvacc[mt][j]);
         }
       }
     }
@@ -650,7 +677,7 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      q_begin, q_len, nqt, table, tile_cnt, tile_list, c2, scale, tmode, (int)total)
 #define GSA_KV(D, TO)                                                                                              \
   hipLaunchKernelGGL((k_bwd_dkdv<D, TO>), dim3((unsigned)((l.nkt + 1) / 2), (unsigned)Hkv, (unsigned)B),        \
-                     dim3(kThreads), 0, s,                                                                       \
+                     dim3(64 * kWaves16), 0, s,                                                                  \
                      l, (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                           \
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                              \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h,                              \
