@@ -50,6 +50,12 @@ template <int D> struct BCfg {
 };
 template <int D> __device__ inline int swz_row(int r) { return r & (D / 8 - 1); }
 template <int D> __device__ inline int swz_tr(int r) { return (4 * (r & 3)) & (D / 8 - 1); }
+// dK/dV stage tiles: read as rows (b128, 8 consecutive rows per phase) and
+// transposed (b64, 4 rows x 16 columns per 16-lane group); both patterns hit
+// distinct 16-byte slots with these (they depend on row % 8 only).
+template <int D> __device__ inline int swz_bw(int r) {
+  return D == 128 ? ((4 * (r & 3)) ^ (2 * ((r >> 2) & 1))) : ((2 * (r & 3)) | ((r >> 2) & 1));
+}
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* glb_void_ptr;
@@ -349,7 +355,7 @@ constexpr int kWaves16 = 8;
 
 // Transposed-read B operand of the 16x16x32 products: 8 bf16 of column
 // d = lane % 16 + 16 mt over the rows base + (e < 4 ? 4 g + e : 16 + 4 g + e - 4),
-// g = lane / 16, of a [rows][D] tile stored in the swz_tr swizzle.
+// g = lane / 16, of a [rows][D] tile stored in the swz_bw swizzle.
 template <int D> __device__ inline bf16x8 tr_pair16(const unsigned short* base, int tr_off, int row0) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + tr_off + row0 * D));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + tr_off + (row0 + 16) * D));
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   int soff[NIW];
 #pragma unroll
-  for (int it = 0; it < NIW; ++it) soff[it] = 8 * (sslot ^ swz_tr<D>((wave * NIW + it) * RPI + srow));
+  for (int it = 0; it < NIW; ++it) soff[it] = 8 * (sslot ^ swz_bw<D>((wave * NIW + it) * RPI + srow));
   // every wave issues exactly NIW * 2 + 1 vector loads per stage (one of them
   // lse or D, or a dummy re-load of lse)
   auto fetch = [&](int r0, int hq, int bi) __attribute__((always_inline)) {
@@ -442,18 +448,19 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
   };
 
   // A-operand row reads (rows 16 t + col, d = 32 ks + 8 g + 0..7; rows 16 t + r
-  // share the swizzle of r) and transposed-read offsets (rows 4 g + col / 4)
+  // share the swizzle of r) and transposed-read offsets (rows 4 g + col / 4;
+  // rows 32 qp + r and 32 qp + 16 + r share it too)
   int ar_off[KS], tr_off[MT];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    ar_off[ks] = col * D + 8 * ((grp + 4 * ks) ^ swz_tr<D>(col));
+    ar_off[ks] = col * D + 8 * ((grp + 4 * ks) ^ swz_bw<D>(col));
     asm volatile("" : "+v"(ar_off[ks]));
   }
   {
     const int trow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      tr_off[mt] = trow * D + 8 * ((2 * mt + ((col & 3) >> 1)) ^ swz_tr<D>(trow)) + 4 * (col & 1);
+      tr_off[mt] = trow * D + 8 * ((2 * mt + ((col & 3) >> 1)) ^ swz_bw<D>(trow)) + 4 * (col & 1);
       asm volatile("" : "+v"(tr_off[mt]));
     }
   }
