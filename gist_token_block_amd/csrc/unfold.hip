@@ -16,6 +16,7 @@
 // starts each row from that partial instead of from zero, so the result is the
 // softmax over the union with no second pass and no double rounding.
 #include "gsa_internal.h"
+#include "select_net.h"
 
 namespace gsa {
 
@@ -87,12 +88,19 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
       for (int e = 0; e < DPL; ++e) acc[hd][e] = 0.f;
     }
     for (int k0 = 0; k0 < nk; k0 += kMaxKeys) {
-      // position of key k0 + lane: the run (chunk) holding it
+      // position of key k0 + lane: the run (chunk) holding it.  When every
+      // chosen chunk unfolds whole (k c keys), key x is raw x % c of chunk x / c.
       int p = -1;
       const int kk = k0 + lane;
-      for (int e = 0; e < l.k && e < 64; ++e) {
-        const int s_e = __shfl(excl, e), l_e = __shfl(len, e), st_e = __shfl(st, e);
-        if (kk >= s_e && kk < s_e + l_e) p = st_e + (kk - s_e);
+      if (nk == l.k * l.c) {
+        const int e = kk / l.c;
+        const int st_e = __shfl(st, imin(e, 63));
+        if (kk < nk) p = st_e + (kk - e * l.c);
+      } else {
+        for (int e = 0; e < l.k && e < 64; ++e) {
+          const int s_e = __shfl(excl, e), l_e = __shfl(len, e), st_e = __shfl(st, e);
+          if (kk >= s_e && kk < s_e + l_e) p = st_e + (kk - s_e);
+        }
       }
       kpos[wave][lane] = p;
       __builtin_amdgcn_wave_barrier();
@@ -137,13 +145,13 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold(
           const float s = p >= 0 ? lg[hd] * c2 : -__builtin_inff();
           float mx = s;
 #pragma unroll
-          for (int j = 32; j > 0; j >>= 1) mx = fmaxf(mx, __shfl_xor(mx, j));
+          for (int j = 32; j > 0; j >>= 1) mx = fmaxf(mx, xor_lane(mx, j));
           const float m_new = fmaxf(m_run[hd], mx);
           const float alpha = __builtin_amdgcn_exp2f(m_run[hd] - m_new);
           const float pr = p >= 0 ? __builtin_amdgcn_exp2f(s - m_new) : 0.f;
           float sum = pr;
 #pragma unroll
-          for (int j = 32; j > 0; j >>= 1) sum += __shfl_xor(sum, j);
+          for (int j = 32; j > 0; j >>= 1) sum += xor_lane(sum, j);
           l_run[hd] = l_run[hd] * alpha + sum;
           m_run[hd] = m_new;
 #pragma unroll
