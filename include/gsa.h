@@ -157,10 +157,12 @@ gsa_status gsa_attn_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k
 /* Top-k selection for many query rows at once (SSA abstract: score the
  * chunks against their gist keys only, keep the k best), the same result as
  * gsa_score_select up to fp32 rounding of the scores: per 128 query rows and
- * KV head, one MFMA pass over the gist stream screens candidates with the
- * group's mean query rounded to bf16, each row keeps its best top_k + 4 or
- * more, and those are ranked by their fp32 scores.  Single level with one
- * gist per chunk, bf16, d in {64, 128}, 1 <= top_k <= 28.
+ * KV head, one MFMA pass over the gist stream scores every candidate with the
+ * sum of the group's query heads split into two bf16 parts (fp32 accuracy;
+ * mean and scale are positive factors and do not change the order), and each
+ * row keeps its k best by (score desc, chunk index asc), a NaN score ranking
+ * as -inf.  Single level with one gist per chunk, bf16, d in {64, 128},
+ * 1 <= top_k <= 32, scale > 0 (GSA_EINVAL otherwise).
  *   q    [B, q_len, Hq, d]; k [B, seq_len, Hkv, d] (by strides)
  *   sel  int32 [B, Hkv, q_len, top_k] (out), ascending, -1 padded */
 gsa_status gsa_select_prefill(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, int32_t B, int32_t Hq,

@@ -1,5 +1,5 @@
 """GPU parity of selective unfolding at prefill scale: gsa_select_prefill
-(MFMA screening + exact fp32 ranking) against the oracle's selection, and
+(MFMA scores at fp32 accuracy, per-row top-k) against the oracle's selection, and
 gsa_attn_prefill_unfolded (unfolded raws attended first, then the MFMA prefill
 of the fixed part starting from that partial) against the oracle's attention
 with the GPU's selection; protocol and tolerances of gsa_testutil."""
@@ -112,3 +112,22 @@ def test_k16_workload_sampled_rows():
     assert_close(o[:, rows], ref[:, rows], TOL["bf16"], bf16_out=True, what="k16 workload")
     assert_close(lse[:, :, rows], ref_lse[:, :, rows], LSE_TOL["bf16"], what="k16 workload lse")
     assert (sel >= -1).all() and (sel < 8192).all()
+
+
+@pytest.mark.parametrize("layout", [dict(n_sink=4, chunk_len=4, gists=1, window=16, top_k=5),
+                                    dict(n_sink=2, chunk_len=3, gists=1, window=8, top_k=20)])
+def test_select_prefill_exact_ties_pick_lowest_chunks(layout):
+    """Every gist key of a KV head equal: all candidates of a row tie, so the
+    (score desc, chunk index asc) rule alone decides, and the kernel must keep
+    each row's lowest chunk indices exactly as the oracle does."""
+    B, Hq, Hkv, d = 1, 4, 2, 128
+    lay = O.Layout.of(layout)
+    L = layout["n_sink"] + 120 * (layout["chunk_len"] + 1) + 2
+    tm = O.type_map(lay, L)
+    q, k, _ = inputs.random_qkv(B, L, Hq, Hkv, d, seed=270, dtype="bf16")
+    gpos = [g[0] for g in tm.chunk_gists if len(g)]
+    k[:, gpos] = k[:, gpos[:1]]
+    scale = 1 / math.sqrt(d)
+    sel = gsa.select_prefill(layout, to_dev(q, "bf16"), to_dev(k, "bf16"), L, 0, scale).cpu().numpy()
+    ref = O.select(lay, tm, q, k, list(range(L)), scale)["sel"]
+    assert (sel == ref).all(), f"{int((sel != ref).any(axis=-1).sum())} rows differ"
