@@ -371,7 +371,7 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
     const unsigned short* __restrict__ dO, int64_t dsb, int64_t dst, int64_t dsh, const float* __restrict__ lse2,
     const float* __restrict__ delta, TO* __restrict__ dk, int64_t ksb_o, int64_t kst_o, int64_t ksh_o,
     TO* __restrict__ dv, int64_t vsb_o, int64_t vst_o, int64_t vsh_o, int Hq, int Hkv, int q_begin, int q_len,
-    int nqt, const int8_t* __restrict__ table, float c2, float scale, int tmode) {
+    int nqt, const int8_t* __restrict__ table, float c2, float scale, int tmode, int npair, int total) {
   constexpr int PPR = D / 8, RPI = 64 / PPR;
   constexpr int NIW = kStage / RPI / kWaves16;   // wave loads per tensor per stage
   constexpr int KS = D / 32;                     // k-steps of S and dP
@@ -384,10 +384,18 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: each XCD (blockIdx % 8) runs a contiguous range of
+  // (batch, KV head, key-tile pair), so the workgroups streaming one KV
+  // group's Q and dO share an L2, and the pairs of sinks and gists, which see
+  // the most query tiles, start first.
+  const int xb = blockIdx.x;
+  const int per = total >> 3, rem = total & 7, xcd = xb & 7;
+  const int logical = xcd * per + imin(xcd, rem) + (xb >> 3);
+  const int pair = logical % npair;
+  const int h = (logical / npair) % Hkv, b = logical / npair / Hkv;
   const int G = Hq / Hkv;
   // key tiles 2 x and 2 x + 1; wave w takes keys [16 (w & 3), + 16) of tile 2 x + (w >> 2)
-  const int kt0 = 2 * blockIdx.x;
+  const int kt0 = 2 * pair;
   const int ktw = kt0 + (wave >> 2);
   const bool tile_ok = ktw < l.nkt;
   int kind = 0, u0 = 0, u1 = 0, slot = 0;
@@ -466,28 +474,30 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
   }
 
   // The stage sequence: query tiles where either tile's code is non-zero,
-  // ascending (scanned 64 at a time by ballot; the codes stay in lanes), then
+  // descending (scanned 64 at a time by ballot; the codes stay in lanes), then
   // every query head of the group, then both 64-row halves.  Every wave walks
-  // the same sequence.
-  int scan0 = 0;
+  // the same sequence.  Descending, the workgroups of sink and gist keys,
+  // which see every later query, all start at the last query tile and move
+  // through Q and dO together, so one copy in L2 serves them all.
+  int scan0 = (nqt - 1) / 64 * 64;
   unsigned long long smask = 0ull;
   int c0v = 0, c1v = 0;   // this lane's codes for query tile scan0 + lane
   int s_qt = -1, s_gq = 0, s_half = 0, s_c0 = 0, s_c1 = 0;
   auto find_tile = [&]() __attribute__((always_inline)) -> bool {
     while (smask == 0ull) {
-      if (scan0 >= nqt) return false;
+      if (scan0 < 0) return false;
       const int qtl = scan0 + lane;
       c0v = qtl < nqt ? col0[(size_t)qtl * l.nkt] : 0;
       c1v = (qtl < nqt && has1) ? col0[(size_t)qtl * l.nkt + 1] : 0;
       smask = __ballot((c0v | c1v) != 0);
-      if (smask == 0ull) scan0 += 64;
+      if (smask == 0ull) scan0 -= 64;
     }
-    const int bit = __builtin_ctzll(smask);
-    smask &= smask - 1ull;
+    const int bit = 63 - __builtin_clzll(smask);
+    smask &= ~(1ull << bit);
     s_qt = scan0 + bit;
     s_c0 = __shfl(c0v, bit);
     s_c1 = __shfl(c1v, bit);
-    if (smask == 0ull) scan0 += 64;
+    if (smask == 0ull) scan0 -= 64;
     return true;
   };
   auto next_stage = [&]() __attribute__((always_inline)) -> bool {
@@ -668,7 +678,8 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
   if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes < %zu", ws_bytes, need);
   const int nqt = (q_len + kBM - 1) / kBM;
   const long long total = (long long)B * Hkv * nqt * (Hq / Hkv);
-  if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
+  const long long kv_total = (long long)B * Hkv * ((l.nkt + 1) / 2);
+  if (total > 0x7fffffff || kv_total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");
   hipStream_t s = (hipStream_t)stream;
   const float c2 = scale * kLog2e;
   float* delta = (float*)ws;                              // D = rowsum(dO O)
@@ -683,14 +694,13 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      dO.stride_h, lse, (TO*)dq.ptr, dq.stride_b, dq.stride_t, dq.stride_h, delta, lse2, Hq, Hkv,   \
                      q_begin, q_len, nqt, table, tile_cnt, tile_list, c2, scale, tmode, (int)total)
 #define GSA_KV(D, TO)                                                                                              \
-  hipLaunchKernelGGL((k_bwd_dkdv<D, TO>), dim3((unsigned)((l.nkt + 1) / 2), (unsigned)Hkv, (unsigned)B),        \
-                     dim3(64 * kWaves16), 0, s,                                                                  \
+  hipLaunchKernelGGL((k_bwd_dkdv<D, TO>), dim3((unsigned)kv_total), dim3(64 * kWaves16), 0, s,                 \
                      l, (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                           \
                      (const unsigned short*)k.ptr, k.stride_b, k.stride_t, k.stride_h,                              \
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h,                              \
                      (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, dO.stride_h, lse2, delta, (TO*)dk.ptr, \
                      dk.stride_b, dk.stride_t, dk.stride_h, (TO*)dv.ptr, dv.stride_b, dv.stride_t, dv.stride_h, Hq, \
-                     Hkv, q_begin, q_len, nqt, table, c2, scale, tmode)
+                     Hkv, q_begin, q_len, nqt, table, c2, scale, tmode, (l.nkt + 1) / 2, (int)kv_total)
 #define GSA_BW(D, TO)                      \
   do {                                     \
     if (of32) GSA_DQ(D, TO, true);         \
