@@ -269,6 +269,9 @@ __global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
   __shared__ int seg_start[65], seg_base[64];
   __shared__ int nseg, am_last;
 
+  // q first: its loads are in flight while the selection is read
+  bf16x8 qreg[C::KS];
+  load_q<D>(a, b, h, qreg);
   // unfolded chunks' raws before the window: one contiguous run per chunk,
   // laid out by an exclusive scan over the selection (lanes of wave 0)
   if (wave == 0) {
@@ -308,8 +311,6 @@ __global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
     pos = seg_base[lo_s] + (v - seg_start[lo_s]);
     fl = kAttend;
   };
-  bf16x8 qreg[C::KS];
-  load_q<D>(a, b, h, qreg);
   const unsigned short* kb = a.kc + b * a.ksb + h * a.ksh;
   const unsigned short* vb = a.vc + b * a.vsb + h * a.vsh;
   const int v_begin = imin(split * a.rpb, total);

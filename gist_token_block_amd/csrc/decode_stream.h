@@ -65,7 +65,10 @@ __device__ void stream_rows(int v_begin, int v_end, RowInfo rowinfo, const unsig
   positions(0);
   if (nblk > 1) positions(1);
   __syncthreads();
+  // the first two blocks are copied at once (both buffers are free), so a
+  // workgroup of one or two blocks waits for a single memory latency
   fetch(0, stage0);
+  if (nblk > 1) fetch(1, stage1);
 
   const int tj = lane & 15;
   const int trow = 4 * grp + (tj >> 2);
@@ -88,12 +91,14 @@ __device__ void stream_rows(int v_begin, int v_end, RowInfo rowinfo, const unsig
     // wave is done with blk - 1 (whose staging buffer the next fetch reuses
     // and whose row-flag slot positions(blk + 2) rewrites: flags rotate over
     // three slots, positions over two), and the row table of blk + 1 is set.
-    __builtin_amdgcn_s_waitcnt(0);
+    // In block 0 the copies of block 1 (2 NIW loads per wave) may still fly.
+    if (blk == 0 && nblk > 1) __builtin_amdgcn_s_waitcnt((2 * C::NIW) | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int fl[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) fl[e] = rowflag[blk % 3][16 * wave + 4 * grp + e];
-    if (blk + 1 < nblk) fetch(blk + 1, next);
+    if (blk >= 1 && blk + 1 < nblk) fetch(blk + 1, next);
     if (blk + 2 < nblk) positions(blk + 2);
     const unsigned short* Vb = Kb + kRows * D;
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
