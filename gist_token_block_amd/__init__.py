@@ -103,7 +103,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gsa_prefill_backward_workspace_bytes.argtypes = [I32, I32, I32]
     lib.gsa_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.gsa_attn_prefill_backward.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor, Tensor, Tensor,
-                                              I32, I32, I32, I32, I32, I32, I32, V, V, V, I32, I32, F, V,
+                                              I32, I32, I32, I32, I32, I32, I32, V, V, V, V, V, I32, I32, F, V,
                                               ctypes.c_size_t, V]
     lib.gsa_attn_prefill_blockmask_backward.argtypes = [Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor, Tensor,
                                                         Tensor, I32, I32, I32, I32, I32, I32, I32, V, V, V, I32, I32,
@@ -501,11 +501,12 @@ def prefill_backward_workspace_bytes(B: int, Hq: int, q_len: int) -> int:
 
 
 def attn_prefill_backward(layout, q, k, v, o, do, lse, tables, block_m: int, block_n: int, q_begin: int = 0,
-                          scale: float | None = None, grad_dtype=torch.float32, workspace=None, out=None):
+                          scale: float | None = None, grad_dtype=torch.float32, workspace=None, out=None,
+                          sel=None, sel_groups=None):
     """dq, dk, dv of the block-sparse prefill.  ``layout`` is a layout dict
-    (fixed layout) or the string "blockmask" (tables of build_block_mask).
+    or the string "blockmask" (tables of build_block_mask).
     ``q``/``do``/``o`` ``[B, Nq, Hq, d]``, ``k``/``v`` ``[B, L, Hkv, d]``,
-    ``lse [B, Hq, Nq]`` from the forward."""
+    ``lse [B, Hq, Nq]``, ``sel``/``sel_groups`` and ``tables`` from the forward."""
     lib = load_library()
     B, Nq, Hq, d = q.shape
     L, Hkv = k.shape[1], k.shape[2]
@@ -521,12 +522,14 @@ def attn_prefill_backward(layout, q, k, v, o, do, lse, tables, block_m: int, blo
         dq, dk, dv = out
     assert lse.dtype == torch.float32 and lse.is_contiguous()
     table, cnt, lst = tables
-    common = (_bthd(q), _bthd(k), _bthd(v), _bthd(o), _bthd(do), lse.data_ptr(), _bthd(dq), _bthd(dk), _bthd(dv),
-              B, Hq, Hkv, d, L, q_begin, Nq, table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m, block_n,
-              float(scale), workspace.data_ptr(), workspace.numel(), _stream())
+    head = (_bthd(q), _bthd(k), _bthd(v), _bthd(o), _bthd(do), lse.data_ptr(), _bthd(dq), _bthd(dk), _bthd(dv),
+            B, Hq, Hkv, d, L, q_begin, Nq)
+    tail = (table.data_ptr(), cnt.data_ptr(), lst.data_ptr(), block_m, block_n, float(scale), workspace.data_ptr(),
+            workspace.numel(), _stream())
     if isinstance(layout, str):
-        assert layout == "blockmask"
-        _check(lib.gsa_attn_prefill_blockmask_backward(*common))
+        assert layout == "blockmask" and sel is None and sel_groups is None
+        _check(lib.gsa_attn_prefill_blockmask_backward(*head, *tail))
     else:
-        _check(lib.gsa_attn_prefill_backward(ctypes.byref(make_layout(layout)), *common))
+        _check(lib.gsa_attn_prefill_backward(ctypes.byref(make_layout(layout)), *head, _ptr(sel), _ptr(sel_groups),
+                                             *tail))
     return dq, dk, dv

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     TO* __restrict__ dq, int64_t gsb, int64_t gst, int64_t gsh, float* __restrict__ delta,
     float* __restrict__ lse2_out, int Hq, int Hkv,
     int q_begin, int q_len, int nqt, const int8_t* __restrict__ table, const int* __restrict__ tile_cnt,
-    const int* __restrict__ tile_list, float c2, float scale, int tmode, int total) {
+    const int* __restrict__ tile_list, const int* __restrict__ sel, const int* __restrict__ selg, float c2,
+    float scale, int tmode, int total) {
   using C = BCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned short K0[kBN * D];
   __shared__ __attribute__((aligned(1024))) unsigned short V0[kBN * D];
@@ -224,9 +225,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     koff[it] = 8 * (sslot ^ swz_tr<D>(row));
     voff[it] = 8 * (sslot ^ swz_row<D>(row));
   }
-  auto fetch = [&](int kt, unsigned short* Kd, unsigned short* Vd, int& kind, int& u0, int& width) {
+  auto fetch = [&](int kt, unsigned short* Kd, unsigned short* Vd, int& slot, int& kind, int& u0, int& width) {
     int u1;
-    const int slot = tile_span(l, kt, kind, u0, u1);
+    slot = tile_span(l, kt, kind, u0, u1);
     width = u1 - u0;
     const StreamMap sm = slot_map(l, slot);
 #pragma unroll
@@ -259,21 +260,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     asm volatile("" : "+v"(tr_off[mt]));
   }
 
-  int nkind = 0, nu0 = 0, nwidth = 0, ncode = 0, kt_next = 0;
+  // the row's selections (layouts with top-k), for PARTIAL tiles whose
+  // visibility depends on them
+  const int* selrow = sel ? sel + (((size_t)b * Hkv + h) * q_len + rr) * l.k : nullptr;
+  const int* selgrow = selg ? selg + (((size_t)b * Hkv + h) * q_len + rr) * l.k2 : nullptr;
+  int nslot = 0, nkind = 0, nu0 = 0, nwidth = 0, ncode = 0, kt_next = 0;
   if (cnt > 0) {
     const int kt0 = list[0];
-    fetch(kt0, K0, V0, nkind, nu0, nwidth);
+    fetch(kt0, K0, V0, nslot, nkind, nu0, nwidth);
     ncode = codes[kt0];
     if (cnt > 1) kt_next = list[1];
   }
 
   auto tile = [&](int idx, const unsigned short* Kb, const unsigned short* Vb, unsigned short* Kn,
                   unsigned short* Vn) {
-    const int kind = nkind, u0 = nu0, width = nwidth, code = ncode;
+    const int slot = nslot, kind = nkind, u0 = nu0, width = nwidth, code = ncode;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (idx + 1 < cnt) {
-      fetch(kt_next, Kn, Vn, nkind, nu0, nwidth);
+      fetch(kt_next, Kn, Vn, nslot, nkind, nu0, nwidth);
       ncode = codes[kt_next];
       if (idx + 2 < cnt) kt_next = list[idx + 2];
     }
@@ -293,14 +298,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     // visibility: slot j of half hf is key 32 hf + 8 (j / 4) + 4 h2 + j % 4
     unsigned vis = 0xffffffffu;
     if (code != 2 || width < kBN) {
-      const int row = wave * 32 + n;
-      const int khi = iclamp(rb[kind][row] - u0, 0, width);
-      const int klo = kind == K_RAW ? iclamp(rlo[row] - u0, 0, width) : 0;
+      // Kinds whose visible keys form one stream range per row (sinks,
+      // level-2 gists, single-level gists, raws without top-k) take the
+      // closed-form bounds; the others follow the row's selection key by key.
+      const bool ranged = kind == K_SINK || kind == K_GIST2 || (kind == K_GIST && l.G2 == 0) ||
+                          (kind == K_RAW && l.k == 0);
       vis = 0;
+      if (code != 0 && ranged) {
+        const int row = wave * 32 + n;
+        const int khi = iclamp(rb[kind][row] - u0, 0, width);
+        const int klo = kind == K_RAW ? iclamp(rlo[row] - u0, 0, width) : 0;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
-        vis |= (unsigned)(key >= klo && key < khi) << j;
+        for (int j = 0; j < 32; ++j) {
+          const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
+          vis |= (unsigned)(key >= klo && key < khi) << j;
+        }
+      } else if (code != 0) {
+        const StreamMap sm = slot_map(l, slot);
+#pragma unroll 1
+        for (int j = 0; j < 32; ++j) {
+          const int key = 32 * (j >> 4) + 8 * ((j & 15) >> 2) + 4 * h2 + (j & 3);
+          bool vv = key < width;
+          if (vv) vv = key_visible(l, i, kind, u0 + key, map_pos(sm, u0 + key), selrow, selgrow);
+          vis |= (unsigned)vv << j;
+        }
       }
     }
     if (!rvalid) vis = 0;
@@ -371,7 +392,8 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
     const unsigned short* __restrict__ dO, int64_t dsb, int64_t dst, int64_t dsh, const float* __restrict__ lse2,
     const float* __restrict__ delta, TO* __restrict__ dk, int64_t ksb_o, int64_t kst_o, int64_t ksh_o,
     TO* __restrict__ dv, int64_t vsb_o, int64_t vst_o, int64_t vsh_o, int Hq, int Hkv, int q_begin, int q_len,
-    int nqt, const int8_t* __restrict__ table, float c2, float scale, int tmode, int npair, int total) {
+    int nqt, const int8_t* __restrict__ table, const int* __restrict__ sel, const int* __restrict__ selg, float c2,
+    float scale, int tmode, int npair, int total) {
   constexpr int PPR = D / 8, RPI = 64 / PPR;
   constexpr int NIW = kStage / RPI / kWaves16;   // wave loads per tensor per stage
   constexpr int KS = D / 32;                     // k-steps of S and dP
@@ -573,15 +595,23 @@ __global__ __launch_bounds__(64 * kWaves16, 1) void k_bwd_dkdv(
       if (needmask) {
         // visibility bits first (bit 4 tt + j), then a select with static
         // indices: no dynamically indexed register write under divergence
+        // Kinds whose visible queries follow closed-form stream ranges use
+        // them; the others test the key against the query row's selection.
+        const bool ranged = kind == K_SINK || kind == K_GIST2 || (kind == K_GIST && l.G2 == 0) ||
+                            (kind == K_RAW && l.k == 0);
+        const size_t srow0 = ((size_t)b * Hkv + h) * q_len;
         unsigned m = 0;
         for (int x = 0; x < 8; ++x) {
           const int rr = r0 + 32 * qp + 16 * (x >> 2) + 4 * grp + (x & 3);
           bool ok = code != 0 && kvalid && rr < q_len;
-          if (ok) {
+          if (ok && ranged) {
             int lo, hi;
             stream_range(l, kind, q_begin + rr, lo, hi);
             const int u = u0 + key;
             ok = u >= lo && u < hi;
+          } else if (ok) {
+            ok = key_visible(l, q_begin + rr, kind, u0 + key, p_key, sel + (srow0 + rr) * l.k,
+                             selg ? selg + (srow0 + rr) * l.k2 : nullptr);
           }
           m |= (unsigned)ok << x;
         }
@@ -651,14 +681,19 @@ namespace {
 gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o,
                            gsa_tensor dO, const float* lse, gsa_tensor dq, gsa_tensor dk, gsa_tensor dv, int32_t B,
                            int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
-                           const int8_t* table, const int32_t* tile_cnt, const int32_t* tile_list,
-                           int32_t block_m, int32_t block_n, float scale, void* ws, size_t ws_bytes, int tmode,
-                           void* stream) {
+                           const int32_t* sel, const int32_t* sel_groups, const int8_t* table,
+                           const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m, int32_t block_n,
+                           float scale, void* ws, size_t ws_bytes, int tmode_in, void* stream) {
   Lay l;
   gsa_status st = make_lay(layout, seq_len, block_n, &l);
   if (st != GSA_OK) return st;
-  if (l.k != 0 || l.G2 != 0)
-    return fail(GSA_EUNSUPPORTED, "the backward takes the fixed layout (top_k = 0, one level) or a block mask");
+  const bool fixed = l.k == 0 && l.G2 == 0;
+  const int tmode = tmode_in == 2 ? 2 : (fixed ? 1 : 0);
+  if (!fixed && !sel) return fail(GSA_EINVAL, "sel is required when top_k > 0");
+  if (fixed && (sel || sel_groups)) return fail(GSA_EINVAL, "sel given for the fixed layout");
+  if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is required with two levels");
+  if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
+  if (l.k > 64 || l.k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
   const char* names[8] = {"q", "k", "v", "o", "do", "dq", "dk", "dv"};
   const gsa_tensor* ts[8] = {&q, &k, &v, &o, &dO, &dq, &dk, &dv};
   for (int e = 0; e < 8; ++e)
@@ -692,7 +727,7 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h, (const void*)o.ptr,        \
                      o.stride_b, o.stride_t, o.stride_h, (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, \
                      dO.stride_h, lse, (TO*)dq.ptr, dq.stride_b, dq.stride_t, dq.stride_h, delta, lse2, Hq, Hkv,   \
-                     q_begin, q_len, nqt, table, tile_cnt, tile_list, c2, scale, tmode, (int)total)
+                     q_begin, q_len, nqt, table, tile_cnt, tile_list, sel, sel_groups, c2, scale, tmode, (int)total)
 #define GSA_KV(D, TO)                                                                                              \
   hipLaunchKernelGGL((k_bwd_dkdv<D, TO>), dim3((unsigned)kv_total), dim3(64 * kWaves16), 0, s,                 \
                      l, (const unsigned short*)q.ptr, q.stride_b, q.stride_t, q.stride_h,                           \
@@ -700,7 +735,8 @@ gsa_status backward_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k,
                      (const unsigned short*)v.ptr, v.stride_b, v.stride_t, v.stride_h,                              \
                      (const unsigned short*)dO.ptr, dO.stride_b, dO.stride_t, dO.stride_h, lse2, delta, (TO*)dk.ptr, \
                      dk.stride_b, dk.stride_t, dk.stride_h, (TO*)dv.ptr, dv.stride_b, dv.stride_t, dv.stride_h, Hq, \
-                     Hkv, q_begin, q_len, nqt, table, c2, scale, tmode, (l.nkt + 1) / 2, (int)kv_total)
+                     Hkv, q_begin, q_len, nqt, table, sel, sel_groups, c2, scale, tmode, (l.nkt + 1) / 2,        \
+                     (int)kv_total)
 #define GSA_BW(D, TO)                      \
   do {                                     \
     if (of32) GSA_DQ(D, TO, true);         \
@@ -732,11 +768,12 @@ extern "C" gsa_status gsa_attn_prefill_backward(const gsa_layout* layout, gsa_te
                                                 gsa_tensor o, gsa_tensor dO, const float* lse, gsa_tensor dq,
                                                 gsa_tensor dk, gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv,
                                                 int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                                                const int32_t* sel, const int32_t* sel_groups,
                                                 const int8_t* table, const int32_t* tile_cnt,
                                                 const int32_t* tile_list, int32_t block_m, int32_t block_n,
                                                 float scale, void* ws, size_t ws_bytes, void* stream) {
-  return backward_common(layout, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, d, seq_len, q_begin, q_len, table,
-                         tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 1, stream);
+  return backward_common(layout, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, d, seq_len, q_begin, q_len, sel,
+                         sel_groups, table, tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 0, stream);
 }
 
 extern "C" gsa_status gsa_attn_prefill_blockmask_backward(gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o,
@@ -753,6 +790,7 @@ extern "C" gsa_status gsa_attn_prefill_blockmask_backward(gsa_tensor q, gsa_tens
   all_sinks.chunk_len = 1;
   all_sinks.gists_per_chunk = 1;
   all_sinks.window = 1;
-  return backward_common(&all_sinks, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, d, seq_len, q_begin, q_len, table,
-                         tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 2, stream);
+  return backward_common(&all_sinks, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, d, seq_len, q_begin, q_len,
+                         nullptr, nullptr, table, tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 2,
+                         stream);
 }

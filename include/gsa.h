@@ -370,19 +370,25 @@ gsa_status gsa_attn_prefill_blockmask(gsa_tensor q, gsa_tensor k, gsa_tensor v, 
  *   q, k, v, do   bf16; o F32 or bf16 (the forward's output); dq, dk, dv F32
  *                 or bf16 (all three alike)
  *   lse           float [B, Hq, q_len], natural log, from the forward
- *   table, tile_cnt, tile_list  the forward's tables (gsa_prefill_tile() shape)
+ *   sel, sel_groups  the forward's selections (as for gsa_attn_prefill): NULL
+ *                 for the fixed layout; sel for top_k > 0; sel_groups too with
+ *                 two levels (GSA_EINVAL when they do not match the layout)
+ *   table, tile_cnt, tile_list  the forward's tables (gsa_prefill_tile() shape;
+ *                 n_tables = 1 for the fixed layout, else B*Hkv)
  *   ws            gsa_prefill_backward_workspace_bytes() bytes (D and the base-2
  *                 log-sum-exp per row are kept there between the two kernels)
  * Every key position of dk and dv is written (zero where no query row sees it).
- * Requires d in {64, 128}.  Layouts: the fixed layout (top_k = 0, one level);
- * other layouts return GSA_EUNSUPPORTED. */
+ * Requires d in {64, 128}.  Any layout; where visibility depends on the
+ * selection, PARTIAL tiles test each key against the query's chosen chunks
+ * (and groups), as the forward does. */
 size_t gsa_prefill_backward_workspace_bytes(int32_t B, int32_t Hq, int32_t q_len);
 gsa_status gsa_attn_prefill_backward(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
                                      gsa_tensor o, gsa_tensor dO, const float* lse, gsa_tensor dq, gsa_tensor dk,
                                      gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t seq_len,
-                                     int32_t q_begin, int32_t q_len, const int8_t* table, const int32_t* tile_cnt,
-                                     const int32_t* tile_list, int32_t block_m, int32_t block_n, float scale,
-                                     void* ws, size_t ws_bytes, void* stream);
+                                     int32_t q_begin, int32_t q_len, const int32_t* sel, const int32_t* sel_groups,
+                                     const int8_t* table, const int32_t* tile_cnt, const int32_t* tile_list,
+                                     int32_t block_m, int32_t block_n, float scale, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* The same backward under a gzip-guided block mask: tables from
  * gsa_build_block_mask (Gzip-guided sparse attention page, Core equations). */

@@ -1,6 +1,7 @@
 """GPU parity of the prefill backward (dq, dk, dv) against the fp64 oracle
 (oracle/gsa_backward.py; the block-mask variant against autograd-free fp64
-formulas over the gzip oracle's mask).
+formulas over the gzip oracle's mask): fixed layouts, layouts with top-k
+unfolding at one and two levels, and block masks.
 
 Inputs are bf16-exact (workloads.inputs), so the oracle sees the same numbers.
 Tolerance (from the arithmetic): the kernels round P and dS to bf16 (relative
@@ -123,7 +124,7 @@ def test_blockmask_backward_all_rows():
     assert_grad_close(dv.cpu().numpy(), rv, "dv blockmask")
 
 
-def test_backward_rejects_selection_layouts():
+def test_backward_selection_layout_needs_sel():
     layout = dict(n_sink=4, chunk_len=4, gists=1, window=16, top_k=2)
     t = torch.zeros((1, 64, 1, 64), dtype=torch.bfloat16, device=dev())
     lse = torch.zeros((1, 1, 64), dtype=torch.float32, device=dev())
@@ -131,7 +132,47 @@ def test_backward_rejects_selection_layouts():
               torch.zeros(1, dtype=torch.int32, device=dev()))
     with pytest.raises(gsa.GsaError) as e:
         gsa.attn_prefill_backward(layout, t, t, t, t, t, lse, tables, 128, 64)
-    assert e.value.status == gsa.GSA_EUNSUPPORTED
+    assert e.value.status == gsa.GSA_EINVAL
+
+
+SEL = [
+    # layout, L, B, Hq, Hkv, d, q_begin: selections from gsa_score_select, one table per (batch, KV head)
+    (dict(n_sink=4, chunk_len=4, gists=1, window=16, top_k=3), 4 + 120 * 5 + 3, 2, 4, 2, 128, 0),
+    (dict(n_sink=2, chunk_len=8, gists=2, window=20, top_k=4), 2 + 50 * 10 + 5, 1, 3, 1, 64, 37),
+    (dict(n_sink=1, chunk_len=2, gists=1, window=3, top_k=5, l2_chunks=4, l2_gists=1, l2_top_k=3),
+     1 + 40 * 13 + 6, 1, 4, 2, 128, 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SEL)))
+def test_backward_selection_layouts_all_rows(case):
+    """Layouts with top-k unfolding (one and two levels): the forward with the
+    GPU's selections and its tables, then the backward with the same, against
+    the fp64 backward oracle over the same selections, every row."""
+    layout, L, B, Hq, Hkv, d, q_begin = SEL[case]
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=500 + case, dtype="bf16")
+    do = inputs.round_bf16(np.random.default_rng(600 + case).standard_normal((B, L, Hq, d), dtype=np.float32))
+    q, do = q[:, q_begin:], do[:, q_begin:]
+    Nq = L - q_begin
+    scale = 1 / math.sqrt(d)
+    tq, tk, tv, tdo = _bf(q), _bf(k), _bf(v), _bf(do)
+    sel, selg, _ = gsa.score_select(layout, tq, tk, L, q_begin, scale)
+    bm, bn = gsa.prefill_tile(torch.bfloat16, d)
+    tables = gsa.build_layout(layout, L, q_begin, Nq, bm, bn, sel, selg, B * Hkv, device=dev())
+    o, lse = gsa.attn_prefill(layout, tq, tk, tv, tables, bm, bn, sel, selg, q_begin, scale,
+                              out_dtype=torch.float32)
+    dq, dk, dv = gsa.attn_prefill_backward(layout, tq, tk, tv, o, tdo, lse, tables, bm, bn, q_begin=q_begin,
+                                           scale=scale, grad_dtype=torch.float32, sel=sel, sel_groups=selg)
+    torch.cuda.synchronize()
+    lay = O.Layout.of(layout)
+    tm = O.type_map(lay, L)
+    s_np = sel.cpu().numpy()
+    g_np = None if selg is None else selg.cpu().numpy()
+    rq, rk, rv, _, _ = GB.attend_backward(lay, tm, q, k, v, do, list(range(q_begin, L)), scale, s_np, g_np)
+    tag = f"selection case {case}"
+    assert_grad_close(dq.cpu().numpy(), rq, "dq " + tag)
+    assert_grad_close(dk.cpu().numpy(), rk, "dk " + tag)
+    assert_grad_close(dv.cpu().numpy(), rv, "dv " + tag)
 
 
 def test_backward_workload_sampled():

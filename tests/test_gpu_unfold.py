@@ -131,3 +131,32 @@ def test_select_prefill_exact_ties_pick_lowest_chunks(layout):
     sel = gsa.select_prefill(layout, to_dev(q, "bf16"), to_dev(k, "bf16"), L, 0, scale).cpu().numpy()
     ref = O.select(lay, tm, q, k, list(range(L)), scale)["sel"]
     assert (sel == ref).all(), f"{int((sel != ref).any(axis=-1).sum())} rows differ"
+
+
+def test_select_prefill_nan_gist_keys_rank_last():
+    """A NaN gist key gives its chunk a NaN score, which ranks below every
+    finite one (as -inf): each row keeps the top-k of its finite candidates,
+    topped up with NaN ones (lowest ids first) where there are too few."""
+    layout = dict(n_sink=2, chunk_len=4, gists=1, window=4, top_k=4)
+    L = 2 + 40 * 5 + 1
+    lay = O.Layout.of(layout)
+    tm = O.type_map(lay, L)
+    q, k, _ = inputs.random_qkv(1, L, 4, 2, 128, seed=21, dtype="bf16")
+    nan_chunks = {1, 3, 17}
+    for m in nan_chunks:
+        k[0, tm.chunk_gists[m][0], :, :] = np.nan
+    scale = 1 / math.sqrt(128)
+    sel = gsa.select_prefill(layout, to_dev(q, "bf16"), to_dev(k, "bf16"), L, 0, scale).cpu().numpy()
+    for h in range(2):
+        for i in range(L):
+            cands = O.chunk_candidates(lay, tm, i)
+            finite = [m for m in cands if m not in nan_chunks]
+            s = O.gist_scores(q[0, i, 2 * h:2 * h + 2], k[0, :, h], tm.chunk_gists, finite, scale)
+            chosen, gap = O.top_k(s, 4)
+            fill = sorted(m for m in cands if m in nan_chunks)[:4 - len(chosen)]
+            want = sorted(chosen + fill) + [-1] * (4 - len(chosen) - len(fill))
+            got = sel[0, h, i].tolist()
+            if got != want:
+                assert gap < 1e-3, f"row {i} head {h}: gpu {got} want {want} (gap {gap:.2e})"
+                picked = [x for x in got if x >= 0]
+                assert len(set(picked)) == len(picked) and set(picked) <= set(cands)
