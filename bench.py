@@ -304,6 +304,54 @@ def run_backward(w, args, torch, gsa, q, k, v):
             "kernels": "k_bwd_dq (also D) + k_bwd_dkdv; bf16 in, bf16 grads"}
 
 
+def run_unfolded_backward(w, args, torch, gsa, q, k, v):
+    """Backward of the selective-unfolding prefill: one forward (untimed:
+    gsa_select_prefill, the fixed table, gsa_attn_prefill_unfolded with the
+    log-sum-exp), then one step = gsa_attn_prefill_unfolded_backward (the fixed
+    part's k_bwd_dq and k_bwd_dkdv, then the unfolded keys' share: dq per query
+    row, the per-chunk lists, dk/dv per chunk).  Algorithmic FLOPs: 10 d per
+    visible (query head, key) pair, unfolded pairs included."""
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    tdo = torch.randn(tq.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bm, bn = gsa.prefill_tile(torch.bfloat16, w.d)
+    scale = 1 / math.sqrt(w.d)
+    sel = gsa.select_prefill(w.layout, tq, tk, w.seq_len, 0, scale)
+    fixed = gsa.build_layout(dict(w.layout, top_k=0), w.seq_len, 0, w.seq_len, bm, bn, device=dev)
+    o, lse = gsa.attn_prefill_unfolded(w.layout, tq, tk, tv, sel, fixed, bm, bn, 0, scale, out_dtype=torch.bfloat16)
+    grads = (torch.empty(tq.shape, dtype=torch.bfloat16, device=dev),
+             torch.empty(tk.shape, dtype=torch.bfloat16, device=dev),
+             torch.empty(tv.shape, dtype=torch.bfloat16, device=dev))
+    ws = torch.empty(gsa.prefill_unfolded_backward_workspace_bytes(w.layout, w.batch, w.hq, w.hkv, w.seq_len,
+                                                                   w.seq_len), dtype=torch.uint8, device=dev)
+
+    def step():
+        gsa.attn_prefill_unfolded_backward(w.layout, tq, tk, tv, o, tdo, lse, sel, fixed, bm, bn, 0, scale,
+                                           workspace=ws, out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(5, args.steps // 2)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    kern_ms = ev[0].elapsed_time(ev[1]) / steps
+    alg = 10.0 * w.d * unfolded_edges(w, sel.cpu().numpy()) * (w.hq // w.hkv)
+    del tq, tk, tv, tdo, o, lse, grads, ws, sel
+    return {"workload": w.name + " (backward)", "ms_per_step": round(wall, 4), "kernel_ms": round(kern_ms, 4),
+            "algorithmic_flops": alg, "tflops_algorithmic": round(alg / (kern_ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(alg / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "k_bwd_dq + k_unfold_bwd_q; k_bwd_dkdv + per-chunk lists + k_unfold_bwd_kv; bf16 grads"}
+
+
 def run_decode(w, args, torch, gsa, copies=4):
     """One decode step = the fused selection + attention (gsa_decode_step);
     caches rotate over `copies` independent buffers so the visible rows are not
@@ -605,7 +653,10 @@ def profile_pass(torch, gsa, args):
     args.warmup, args.steps = 1, 1
     if args.pass_backward:
         q, k, v = inputs.prefill_inputs(w, seed=1)
-        run_backward(w, args, torch, gsa, q, k, v)
+        if w.top_k > 0:
+            run_unfolded_backward(w, args, torch, gsa, q, k, v)
+        else:
+            run_backward(w, args, torch, gsa, q, k, v)
     elif w.kind == "blockmask":
         run_blockmask(w, args, torch, gsa)
     elif w.kind == "prefill":
@@ -712,6 +763,13 @@ def main():
         log(f"backward {wbk.name}: {pbk['ms_per_step']:.3f} ms/step, kernels {pbk['kernel_ms']:.3f} ms "
             f"({pbk['tflops_algorithmic']} TFLOP/s algorithmic)")
         out.setdefault("prefill", []).append(pbk)
+        wuk = configs.LLAMA3B_K16_PREFILL
+        q, k, v = inputs.prefill_inputs(wuk, seed=1)
+        puk = run_unfolded_backward(wuk, args, torch, gsa, q, k, v)
+        del q, k, v
+        log(f"backward {wuk.name}: {puk['ms_per_step']:.3f} ms/step ({puk['tflops_algorithmic']} TFLOP/s "
+            f"algorithmic)")
+        out["prefill"].append(puk)
     if not args.no_blockmask:
         wb = configs.GZIP_BLOCKMASK_PREFILL
         pb = run_blockmask(wb, args, torch, gsa)

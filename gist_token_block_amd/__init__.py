@@ -48,7 +48,8 @@ EXPORTS = ("gsa_table_dims", "gsa_build_layout", "gsa_score_select", "gsa_score_
            "gsa_compact_decode_workspace_bytes", "gsa_select_prefill", "gsa_attn_prefill_unfolded",
            "gsa_prefill_unfolded_workspace_bytes", "gsa_gzip_block_flags", "gsa_build_block_mask",
            "gsa_attn_prefill_blockmask", "gsa_prefill_backward_workspace_bytes", "gsa_attn_prefill_backward",
-           "gsa_attn_prefill_blockmask_backward", "gsa_status_str", "gsa_last_error")
+           "gsa_attn_prefill_blockmask_backward", "gsa_prefill_unfolded_backward_workspace_bytes",
+           "gsa_attn_prefill_unfolded_backward", "gsa_status_str", "gsa_last_error")
 
 _lib = None
 
@@ -108,6 +109,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gsa_attn_prefill_blockmask_backward.argtypes = [Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor, Tensor,
                                                         Tensor, I32, I32, I32, I32, I32, I32, I32, V, V, V, I32, I32,
                                                         F, V, ctypes.c_size_t, V]
+    lib.gsa_prefill_unfolded_backward_workspace_bytes.argtypes = [LP, I32, I32, I32, I32, I32]
+    lib.gsa_prefill_unfolded_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.gsa_attn_prefill_unfolded_backward.argtypes = [LP, Tensor, Tensor, Tensor, Tensor, Tensor, V, Tensor,
+                                                       Tensor, Tensor, I32, I32, I32, I32, I32, I32, I32, V, V, V, V,
+                                                       I32, I32, F, V, ctypes.c_size_t, V]
     lib.gsa_status_str.argtypes = [I32]
     lib.gsa_status_str.restype = ctypes.c_char_p
     lib.gsa_last_error.argtypes = []
@@ -116,7 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         if name not in ("gsa_score_columns", "gsa_decode_workspace_bytes", "gsa_status_str",
                         "gsa_last_error", "gsa_decode_step_workspace_bytes", "gsa_compact_slots",
                         "gsa_compact_gists", "gsa_compact_decode_workspace_bytes",
-                        "gsa_prefill_unfolded_workspace_bytes", "gsa_prefill_backward_workspace_bytes"):
+                        "gsa_prefill_unfolded_workspace_bytes", "gsa_prefill_backward_workspace_bytes",
+                        "gsa_prefill_unfolded_backward_workspace_bytes"):
             getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -498,6 +505,40 @@ def attn_prefill_blockmask(q, k, v, tables, block_m: int, block_n: int, q_begin:
 
 def prefill_backward_workspace_bytes(B: int, Hq: int, q_len: int) -> int:
     return int(load_library().gsa_prefill_backward_workspace_bytes(B, Hq, q_len))
+
+
+def prefill_unfolded_backward_workspace_bytes(layout: dict, B: int, Hq: int, Hkv: int, seq_len: int,
+                                              q_len: int) -> int:
+    return int(load_library().gsa_prefill_unfolded_backward_workspace_bytes(ctypes.byref(make_layout(layout)), B,
+                                                                            Hq, Hkv, seq_len, q_len))
+
+
+def attn_prefill_unfolded_backward(layout: dict, q, k, v, o, do, lse, sel, fixed_tables, block_m: int,
+                                   block_n: int, q_begin: int = 0, scale: float | None = None,
+                                   grad_dtype=torch.float32, workspace=None, out=None):
+    """dq, dk, dv of attn_prefill_unfolded: ``fixed_tables`` are the fixed
+    layout's (top_k = 0) tables, ``o``/``lse`` the unfolded forward's."""
+    lib = load_library()
+    B, Nq, Hq, d = q.shape
+    L, Hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if workspace is None:
+        need = prefill_unfolded_backward_workspace_bytes(layout, B, Hq, Hkv, L, Nq)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq = torch.empty((B, Nq, Hq, d), dtype=grad_dtype, device=q.device)
+        dk = torch.empty((B, L, Hkv, d), dtype=grad_dtype, device=q.device)
+        dv = torch.empty((B, L, Hkv, d), dtype=grad_dtype, device=q.device)
+    else:
+        dq, dk, dv = out
+    assert lse.dtype == torch.float32 and lse.is_contiguous()
+    table, cnt, lst = fixed_tables
+    _check(lib.gsa_attn_prefill_unfolded_backward(
+        ctypes.byref(make_layout(layout)), _bthd(q), _bthd(k), _bthd(v), _bthd(o), _bthd(do), lse.data_ptr(),
+        _bthd(dq), _bthd(dk), _bthd(dv), B, Hq, Hkv, d, L, q_begin, Nq, sel.data_ptr(), table.data_ptr(),
+        cnt.data_ptr(), lst.data_ptr(), block_m, block_n, float(scale), workspace.data_ptr(), workspace.numel(),
+        _stream()))
+    return dq, dk, dv
 
 
 def attn_prefill_backward(layout, q, k, v, o, do, lse, tables, block_m: int, block_n: int, q_begin: int = 0,

@@ -794,3 +794,64 @@ extern "C" gsa_status gsa_attn_prefill_blockmask_backward(gsa_tensor q, gsa_tens
                          nullptr, nullptr, table, tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 2,
                          stream);
 }
+
+namespace gsa {
+size_t unfold_backward_extra_bytes(const Lay& l, int B, int Hkv, int q_len, int nch);
+gsa_status launch_unfold_backward(const Lay& l, int d, const gsa_tensor& q, const gsa_tensor& k, const gsa_tensor& v,
+                                  const gsa_tensor& dO, const gsa_tensor& dq, const gsa_tensor& dk,
+                                  const gsa_tensor& dv, int B, int Hq, int Hkv, int q_begin, int q_len,
+                                  const int* sel, int nch, float scale, const float* lse2, const float* delta,
+                                  char* extra, hipStream_t st, int phase);
+}  // namespace gsa
+
+namespace {
+size_t fixed_part_bytes(int B, int Hq, int q_len) { return (2 * (size_t)B * Hq * q_len * sizeof(float) + 255) / 256 * 256; }
+}  // namespace
+
+extern "C" size_t gsa_prefill_unfolded_backward_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq,
+                                                                int32_t Hkv, int32_t seq_len, int32_t q_len) {
+  Lay l;
+  if (!layout || make_lay(layout, seq_len, 64, &l) != GSA_OK || B < 1 || Hq < 1 || Hkv < 1 || q_len < 0 || l.k < 1)
+    return 0;
+  const int nch = count_below(l, K_GIST, seq_len) / l.g;
+  return fixed_part_bytes(B, Hq, q_len) + unfold_backward_extra_bytes(l, B, Hkv, q_len, imax(nch, 1));
+}
+
+extern "C" gsa_status gsa_attn_prefill_unfolded_backward(
+    const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v, gsa_tensor o, gsa_tensor dO,
+    const float* lse, gsa_tensor dq, gsa_tensor dk, gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+    int32_t seq_len, int32_t q_begin, int32_t q_len, const int32_t* sel, const int8_t* table,
+    const int32_t* tile_cnt, const int32_t* tile_list, int32_t block_m, int32_t block_n, float scale, void* ws,
+    size_t ws_bytes, void* stream) {
+  if (!layout) return fail(GSA_EINVAL, "layout is NULL");
+  Lay l;
+  gsa_status st = make_lay(layout, seq_len, block_n, &l);
+  if (st != GSA_OK) return st;
+  if (l.G2 != 0) return fail(GSA_EUNSUPPORTED, "the unfolded backward takes one level");
+  if (l.k < 1) return fail(GSA_EINVAL, "top_k must be >= 1 (the fixed layout needs no unfolding)");
+  if (!sel) return fail(GSA_EINVAL, "sel is NULL");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(GSA_EINVAL, "bad head counts B=%d Hq=%d Hkv=%d", B, Hq, Hkv);
+  if (q_len < 1) return fail(GSA_EINVAL, "q_len %d < 1", q_len);
+  const size_t need = gsa_prefill_unfolded_backward_workspace_bytes(layout, B, Hq, Hkv, seq_len, q_len);
+  if (need == 0) return fail(GSA_EINVAL, "bad sizes for the unfolded backward");
+  if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
+  // the fixed part (sinks, earlier gists, window) on the fixed layout's tables
+  gsa_layout fixed_layout = *layout;
+  fixed_layout.top_k = 0;
+  if ((st = backward_common(&fixed_layout, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, d, seq_len, q_begin, q_len,
+                            nullptr, nullptr, table, tile_cnt, tile_list, block_m, block_n, scale, ws, ws_bytes, 0,
+                            stream)) != GSA_OK)
+    return st;
+  // then the unfolded keys' share, from the fixed part's D and base-2 lse
+  const float* delta = (const float*)ws;
+  const float* lse2 = delta + (size_t)B * Hq * q_len;
+  char* extra = (char*)ws + fixed_part_bytes(B, Hq, q_len);
+  const int nch = imax(1, count_below(l, K_GIST, seq_len) / l.g);
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = launch_unfold_backward(l, d, q, k, v, dO, dq, dk, dv, B, Hq, Hkv, q_begin, q_len, sel, nch, scale, lse2,
+                                   delta, extra, s, 0)) != GSA_OK)
+    return st;
+  return launch_unfold_backward(l, d, q, k, v, dO, dq, dk, dv, B, Hq, Hkv, q_begin, q_len, sel, nch, scale, lse2,
+                                delta, extra, s, 1);
+}

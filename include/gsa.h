@@ -400,6 +400,31 @@ gsa_status gsa_attn_prefill_blockmask_backward(gsa_tensor q, gsa_tensor k, gsa_t
                                                int32_t block_n, float scale, void* ws, size_t ws_bytes,
                                                void* stream);
 
+/* The backward of gsa_attn_prefill_unfolded (selective unfolding at scale:
+ * SSA abstract; GSA abstract, trained end to end).  A query's keys split into
+ * the fixed part and its unfolded raws, disjoint, so: the fixed part's
+ * gradients come from the fixed layout's tables as in gsa_attn_prefill_backward,
+ * then the unfolded keys add theirs -- to dq from each query's gathered raws,
+ * to dk and dv per chunk over the query rows that unfolded it (a per-chunk
+ * list in the workspace, walked in ascending row order).  P is recomputed
+ * from the forward's log-sum-exp over the union.
+ *   layout   single level, top_k >= 1; sel as given to the forward
+ *   table, tile_cnt, tile_list  the fixed layout's tables (top_k = 0), as
+ *            gsa_attn_prefill_unfolded takes them
+ *   o, lse   the unfolded forward's output and log-sum-exp
+ *   other arguments and dtypes as gsa_attn_prefill_backward; chunk_len <= 16
+ *   ws       gsa_prefill_unfolded_backward_workspace_bytes() bytes, 256-byte
+ *            aligned (D, the base-2 lse and the per-chunk lists) */
+size_t gsa_prefill_unfolded_backward_workspace_bytes(const gsa_layout* layout, int32_t B, int32_t Hq, int32_t Hkv,
+                                                     int32_t seq_len, int32_t q_len);
+gsa_status gsa_attn_prefill_unfolded_backward(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, gsa_tensor v,
+                                              gsa_tensor o, gsa_tensor dO, const float* lse, gsa_tensor dq,
+                                              gsa_tensor dk, gsa_tensor dv, int32_t B, int32_t Hq, int32_t Hkv,
+                                              int32_t d, int32_t seq_len, int32_t q_begin, int32_t q_len,
+                                              const int32_t* sel, const int8_t* table, const int32_t* tile_cnt,
+                                              const int32_t* tile_list, int32_t block_m, int32_t block_n, float scale,
+                                              void* ws, size_t ws_bytes, void* stream);
+
 const char* gsa_status_str(gsa_status status);
 
 /* Message of the last non-OK return on the calling thread ("" if none). */

@@ -199,3 +199,78 @@ def test_backward_workload_sampled():
         _, rk, rv, _, _ = GB.attend_backward(lay, tm, q[:, wrows], k, v, do[:, wrows], wrows, scale)
         assert_grad_close(dk[:, p], rk[:, p], f"dk raw key {p}")
         assert_grad_close(dv[:, p], rv[:, p], f"dv raw key {p}")
+
+
+UNF = [
+    # layout, L, B, Hq, Hkv, d, q_begin: the unfolded forward and its backward
+    (dict(n_sink=4, chunk_len=4, gists=1, window=16, top_k=3), 4 + 200 * 5 + 3, 2, 6, 2, 128, 0),
+    (dict(n_sink=16, chunk_len=8, gists=1, window=40, top_k=16), 16 + 120 * 9 + 5, 1, 4, 2, 128, 0),
+    (dict(n_sink=2, chunk_len=3, gists=2, window=7, top_k=8), 2 + 150 * 5 + 1, 1, 8, 2, 64, 101),
+]
+
+
+def _unfolded_forward_backward(layout, q, k, v, do, q_begin, grad_dtype):
+    B, Nq, Hq, d = q.shape
+    L = k.shape[1]
+    scale = 1 / math.sqrt(d)
+    tq, tk, tv, tdo = _bf(q), _bf(k), _bf(v), _bf(do)
+    if layout["gists"] == 1:
+        sel = gsa.select_prefill(layout, tq, tk, L, q_begin, scale)
+    else:   # the prefill-scale selection takes one gist per chunk
+        sel = gsa.score_select(layout, tq, tk, L, q_begin, scale)[0]
+    bm, bn = gsa.prefill_tile(torch.bfloat16, d)
+    fixed = gsa.build_layout(dict(layout, top_k=0), L, q_begin, Nq, bm, bn, device=dev())
+    o, lse = gsa.attn_prefill_unfolded(layout, tq, tk, tv, sel, fixed, bm, bn, q_begin, scale,
+                                       out_dtype=torch.float32)
+    dq, dk, dv = gsa.attn_prefill_unfolded_backward(layout, tq, tk, tv, o, tdo, lse, sel, fixed, bm, bn, q_begin,
+                                                    scale, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), dq.float().cpu().numpy(), dk.float().cpu().numpy(), dv.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("case", range(len(UNF)))
+@pytest.mark.parametrize("grad_dtype", [torch.float32, torch.bfloat16])
+def test_unfolded_backward_small_all_rows(case, grad_dtype):
+    """gsa_attn_prefill_unfolded_backward against the fp64 backward oracle with
+    the GPU's selections, every row (ragged tails, a query offset, d 64)."""
+    layout, L, B, Hq, Hkv, d, q_begin = UNF[case]
+    q, k, v = inputs.random_qkv(B, L, Hq, Hkv, d, seed=700 + case, dtype="bf16")
+    do = inputs.round_bf16(np.random.default_rng(800 + case).standard_normal((B, L, Hq, d), dtype=np.float32))
+    q, do = q[:, q_begin:], do[:, q_begin:]
+    sel, dq, dk, dv = _unfolded_forward_backward(layout, q, k, v, do, q_begin, grad_dtype)
+    lay = O.Layout.of(layout)
+    tm = O.type_map(lay, L)
+    rq, rk, rv, _, _ = GB.attend_backward(lay, tm, q, k, v, do, list(range(q_begin, L)), 1 / math.sqrt(d), sel)
+    tag = f"unfolded case {case} {grad_dtype}"
+    assert_grad_close(dq, rq, "dq " + tag)
+    assert_grad_close(dk, rk, "dk " + tag)
+    assert_grad_close(dv, rv, "dv " + tag)
+
+
+def test_unfolded_backward_k16_workload_sampled():
+    """The 3B-shape 32K workload with per-query top-16 unfolding: dq of sampled
+    rows, and dk/dv of sampled raw keys far from the window's reach, which the
+    oracle evaluates over every row that sees them (their window and the rows
+    whose selection unfolds their chunk)."""
+    w = configs.LLAMA3B_K16_PREFILL
+    L = w.seq_len
+    q, k, v = inputs.prefill_inputs(w, seed=21)
+    do = inputs.round_bf16(np.random.default_rng(22).standard_normal((w.batch, L, w.hq, w.d), dtype=np.float32))
+    sel, dq, dk, dv = _unfolded_forward_backward(w.layout, q, k, v, do, 0, torch.float32)
+    lay = O.Layout.of(w.layout)
+    tm = O.type_map(lay, L)
+    scale = 1 / math.sqrt(w.d)
+    rng = np.random.default_rng(23)
+    rows = sorted(set(rng.integers(0, L, 5).tolist()) | {L - 1})
+    rq, _, _, _, _ = GB.attend_backward(lay, tm, q[:, rows], k, v, do[:, rows], rows, scale, sel[:, :, rows])
+    assert_grad_close(dq[:, rows], rq, "dq k16 rows")
+    typ = np.asarray(tm.typ)
+    raws = np.nonzero(typ == O.RAW)[0]
+    for p in [int(x) for x in rng.choice(raws[(raws > 4000) & (raws < 30000)], 2, replace=False)]:
+        chunk = int(tm.chunk[p])
+        see = set(range(p, min(L, p + w.window)))
+        see |= set(np.nonzero((sel[0] == chunk).any(axis=-1))[1].tolist())
+        rr = sorted(see)
+        _, rk, rv, _, _ = GB.attend_backward(lay, tm, q[:, rr], k, v, do[:, rr], rr, scale, sel[:, :, rr])
+        assert_grad_close(dk[:, p], rk[:, p], f"dk raw key {p}")
+        assert_grad_close(dv[:, p], rv[:, p], f"dv raw key {p}")
