@@ -307,15 +307,16 @@ __global__ void k_chunk_fill(Lay l, const int* __restrict__ sel, int B, int Hkv,
 }
 
 // ------------------------------------------------------------------ dK, dV
-// CM (a power of two, 2 .. 16) bounds the raws per chunk.  Lane layout: key t
-// of the chunk = lane / (64 / CM), and that key's DPG = D CM / 64 dimensions
-// starting at DPG (lane % (64 / CM)) -- so a dot product reduces over 64 / CM
-// lanes only, and every key of the chunk advances at once.  The (row, head)
-// pairs of a chunk go in batches of KP (8 at most, fewer as the dimensions per
-// lane grow): lane j of the batch looks up pair j's row, head, log-sum-exp and
-// D, the wave takes them from that lane (so the q and dO rows are addressed
-// with wave-uniform bases), and every q and dO load of the batch is issued,
-// still packed, before the first product.
+// CM (a power of two, 2 .. 16) bounds the raws per chunk.  Lane layout: the
+// wave holds S = 2048 / (D CM) (row, query head) pairs at once, one per slot
+// of LS = 64 / S lanes; a lane owns DL = 32 / CM dimensions of its slot's
+// pair and of every raw of the chunk, so each load fetches distinct bytes and
+// one q or dO load instruction covers S pairs.  Logits and dP are packed bf16
+// dot products summed over the slot's lanes; each lane accumulates its
+// dimensions of dK and dV for every raw, and the slots' sums are added at the
+// end.  Pairs go in batches of KP steps: the lanes of a slot look up the
+// rows, heads, log-sum-exps and D of the batch's pairs, and every q and dO
+// load of the batch is issued, packed, before the first product.
 
 template <int N> __device__ inline void load_words(const unsigned short* p, unsigned (&w)[N]) {
   if constexpr (N % 4 == 0) {
@@ -335,15 +336,41 @@ template <int N> __device__ inline void load_words(const unsigned short* p, unsi
   }
 }
 
-template <int LPK> __device__ inline float group_sum(float v) {
-#pragma unroll
-  for (int j = 1; j < LPK; j <<= 1) v += xor_lane(v, j);
+template <int CTRL> __device__ inline float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LS lanes of a slot (aligned groups of LS lanes), in every lane.
+template <int LS> __device__ inline float slot_sum(float v) {
+  if constexpr (LS >= 16) {
+    v = dpp_add<0x128>(v);   // row_ror:8 (rotations within a 16-lane row reduce it in 4 steps)
+    v = dpp_add<0x124>(v);   // row_ror:4
+    v = dpp_add<0x122>(v);   // row_ror:2
+    v = dpp_add<0x121>(v);   // row_ror:1
+    if constexpr (LS >= 32) v += xor_lane(v, 16);
+    if constexpr (LS >= 64) v += xor_lane(v, 32);
+  } else if constexpr (LS == 8) {
+    v = dpp_add<0x141>(v);   // row_half_mirror: lane i + lane 7 - i
+    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  } else if constexpr (LS == 4) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+  } else {
+    static_assert(LS == 2, "slots of 2 .. 64 lanes");
+    v = dpp_add<0xB1>(v);
+  }
   return v;
 }
 
-__device__ inline int lane_int(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
-__device__ inline float lane_float(float v, int j) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+// Sum over the slots of the lanes at the same place in each slot.
+template <int LS> __device__ inline float cross_slot_sum(float v) {
+  if constexpr (LS <= 8) v = dpp_add<0x128>(v);   // row_ror:8
+  if constexpr (LS <= 4) v = dpp_add<0x124>(v);   // row_ror:4
+  if constexpr (LS <= 2) v = dpp_add<0x122>(v);   // row_ror:2
+  if constexpr (LS <= 16) v += xor_lane(v, 16);
+  if constexpr (LS <= 32) v += xor_lane(v, 32);
+  return v;
 }
 
 template <int D, int CM, typename TG>
@@ -356,14 +383,16 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold_bwd_kv(
     int64_t kst_o, int64_t ksh_o, TG* __restrict__ dv, int64_t vsb_o, int64_t vst_o, int64_t vsh_o, int B, int Hq,
     int Hkv, int q_begin, int q_len, int nch, const int* __restrict__ off, const int* __restrict__ list, float c2,
     float scale) {
-  constexpr int LPK = 64 / CM;    // lanes per key
-  constexpr int DPG = D / LPK;    // dimensions per lane
-  constexpr int NW = DPG / 2;     // packed bf16 words per lane and row
-  constexpr int KP = NW <= 4 ? 8 : 32 / NW;
+  constexpr int DL = 32 / CM;                 // dimensions per lane
+  constexpr int NW = DL / 2;                  // packed bf16 words per lane and row
+  constexpr int LS = D / DL;                  // lanes per slot
+  constexpr int S = 64 / LS;                  // pairs per step
+  constexpr int KP = LS < 8 ? LS : (DL > 8 ? 4 : 8);   // steps per batch (at most LS: one lookup lane each)
+  static_assert(LS * S == 64 && LS >= 2, "D * CM between 128 and 2048");
   __shared__ int seg[kWaves][kSortCap];
   __shared__ int srt[kWaves][kSortCap];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = lane / LPK, d0 = DPG * (lane % LPK);   // this lane's key and first dimension
+  const int slot = lane / LS, sl = lane % LS, d0 = DL * sl;
   const int G = Hq / Hkv;
   const int C = imin(l.c, CM);
   const long long total = (long long)B * Hkv * nch;
@@ -393,81 +422,104 @@ __global__ __launch_bounds__(64 * kWaves) void k_unfold_bwd_kv(
       __builtin_amdgcn_wave_barrier();
     }
     const int st = pos_of(l, K_RAW, m * l.c);
-    const int tk = imin(t, C - 1);   // lanes of keys past the chunk re-read its last raw (their P is 0)
-    float kd[DPG], vd[DPG], gk[DPG], gv[DPG];
-    {
-      unsigned kw[NW], vw[NW];
-      load_words<NW>(k + b * ksb + (int64_t)(st + tk) * kst + h * ksh + d0, kw);
-      load_words<NW>(v + b * vsb + (int64_t)(st + tk) * vst + h * vsh + d0, vw);
+    // this lane's dimensions of every raw of the chunk (raws past its end
+    // re-read the last one; their P is 0)
+    unsigned kw[CM][NW], vw[CM][NW];
 #pragma unroll
-      for (int e = 0; e < NW; ++e) {
-        kd[2 * e] = lo_bf16(kw[e]);
-        kd[2 * e + 1] = hi_bf16(kw[e]);
-        vd[2 * e] = lo_bf16(vw[e]);
-        vd[2 * e + 1] = hi_bf16(vw[e]);
-      }
+    for (int t = 0; t < CM; ++t) {
+      const int row = st + imin(t, C - 1);
+      load_words<NW>(k + b * ksb + (int64_t)row * kst + h * ksh + d0, kw[t]);
+      load_words<NW>(v + b * vsb + (int64_t)row * vst + h * vsh + d0, vw[t]);
     }
+    float gk[CM][DL], gv[CM][DL];
 #pragma unroll
-    for (int e = 0; e < DPG; ++e) gk[e] = gv[e] = 0.f;
+    for (int t = 0; t < CM; ++t)
+#pragma unroll
+      for (int e = 0; e < DL; ++e) gk[t][e] = gv[t][e] = 0.f;
     const int npair = n * G;
     const int64_t qb = b * qsb + (int64_t)h * G * qsh + d0, ob = b * dsb + (int64_t)h * G * dsh + d0;
-    for (int p0 = 0; p0 < npair; p0 += KP) {
-      // lane j < KP: pair p0 + j (the last pair again past the end)
-      int rr = 0, hh = 0;
+    for (int p0 = 0; p0 < npair; p0 += KP * S) {
+      // lane sl < KP of each slot: pair p0 + sl S + slot (row * 16 + head, -1 past the end)
+      int rh = -1;
       float l2v = 0.f, dlv = 0.f;
-      if (lane < KP) {
-        const int pj = imin(p0 + lane, npair - 1);
-        const int x = pj / G;
-        hh = pj - x * G;
-        rr = sorted ? srt[wave][x] : rows[x];
-        const size_t ri = ((size_t)b * Hq + h * G + hh) * q_len + rr;
-        l2v = lse2[ri];
-        dlv = delta[ri];
+      if (sl < KP) {
+        const int pid = p0 + sl * S + slot;
+        if (pid < npair) {
+          const int x = pid / G, hd = pid - x * G;
+          const int r = sorted ? srt[wave][x] : rows[x];
+          rh = r * 16 + hd;
+          const size_t ri = ((size_t)b * Hq + h * G + hd) * q_len + r;
+          l2v = lse2[ri];
+          dlv = delta[ri];
+        }
       }
       unsigned qw[KP][NW], ow[KP][NW];
+      int rhj[KP];
 #pragma unroll
       for (int j = 0; j < KP; ++j) {
-        const int r = lane_int(rr, j), hd = lane_int(hh, j);
+        rhj[j] = __shfl(rh, slot * LS + j);
+        const int x = imax(rhj[j], 0), r = x >> 4, hd = x & 15;
         load_words<NW>(q + qb + (int64_t)r * qst + (int64_t)hd * qsh, qw[j]);
         load_words<NW>(dO + ob + (int64_t)r * dst + (int64_t)hd * dsh, ow[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < KP; ++j) {
-        const int r = lane_int(rr, j);
-        // this lane's raw lies before the row's window (none for the padding)
-        const bool vis = p0 + j < npair && t < C && st + t < q_begin + r - l.W1 + 1;
-        float a = 0.f, c = 0.f, qf[DPG], of[DPG];
+        const float l2 = __shfl(l2v, slot * LS + j), dl = __shfl(dlv, slot * LS + j);
+        float sc[CM], dp[CM];
 #pragma unroll
-        for (int e = 0; e < NW; ++e) {
-          qf[2 * e] = lo_bf16(qw[j][e]);
-          qf[2 * e + 1] = hi_bf16(qw[j][e]);
-          of[2 * e] = lo_bf16(ow[j][e]);
-          of[2 * e + 1] = hi_bf16(ow[j][e]);
+        for (int t = 0; t < CM; ++t) {
+          float a = 0.f, c = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[j][w]),
+                                                __builtin_bit_cast(bf16x2, kw[t][w]), a, false);
+            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ow[j][w]),
+                                                __builtin_bit_cast(bf16x2, vw[t][w]), c, false);
+          }
+          sc[t] = slot_sum<LS>(a);
+          dp[t] = slot_sum<LS>(c);
         }
+        float qf[DL], of[DL];
 #pragma unroll
-        for (int e = 0; e < DPG; ++e) {
-          a = fmaf(qf[e], kd[e], a);
-          c = fmaf(of[e], vd[e], c);
+        for (int w = 0; w < NW; ++w) {
+          qf[2 * w] = lo_bf16(qw[j][w]);
+          qf[2 * w + 1] = hi_bf16(qw[j][w]);
+          of[2 * w] = lo_bf16(ow[j][w]);
+          of[2 * w + 1] = hi_bf16(ow[j][w]);
         }
-        const float sp = group_sum<LPK>(a), pp = group_sum<LPK>(c);
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(sp, c2, -lane_float(l2v, j))) : 0.f;
-        const float ds = scale * pr * (pp - lane_float(dlv, j));
+        // raw t lies before the row's window (none for the padding)
+        const int lim = rhj[j] >= 0 ? q_begin + (rhj[j] >> 4) - l.W1 + 1 - st : 0;
 #pragma unroll
-        for (int e = 0; e < DPG; ++e) {
-          gk[e] = fmaf(ds, qf[e], gk[e]);
-          gv[e] = fmaf(pr, of[e], gv[e]);
+        for (int t = 0; t < CM; ++t) {
+          const bool vis = t < C && t < lim;
+          const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(sc[t], c2, -l2)) : 0.f;
+          const float ds = scale * pr * (dp[t] - dl);
+#pragma unroll
+          for (int e = 0; e < DL; ++e) {
+            gk[t][e] = fmaf(ds, qf[e], gk[t][e]);
+            gv[t][e] = fmaf(pr, of[e], gv[t][e]);
+          }
         }
       }
     }
-    // add to the fixed part's dk and dv
-    if (t < C) {
-      TG* kr = dk + b * ksb_o + (int64_t)(st + t) * kst_o + h * ksh_o + d0;
-      TG* vr = dv + b * vsb_o + (int64_t)(st + t) * vst_o + h * vsh_o + d0;
+    // add the slots' sums to the fixed part's dk and dv; slot s writes the
+    // raws t with t mod S = s
 #pragma unroll
-      for (int e = 0; e < DPG; ++e) {
-        GradIO<TG>::put(kr + e, GradIO<TG>::get(kr + e) + gk[e]);
-        GradIO<TG>::put(vr + e, GradIO<TG>::get(vr + e) + gv[e]);
+    for (int t = 0; t < CM; ++t) {
+#pragma unroll
+      for (int e = 0; e < DL; ++e) {
+        gk[t][e] = cross_slot_sum<LS>(gk[t][e]);
+        gv[t][e] = cross_slot_sum<LS>(gv[t][e]);
+      }
+      if (t < C && t % S == slot) {
+        TG* kr = dk + b * ksb_o + (int64_t)(st + t) * kst_o + h * ksh_o + d0;
+        TG* vr = dv + b * vsb_o + (int64_t)(st + t) * vst_o + h * vsh_o + d0;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+          GradIO<TG>::put(kr + e, GradIO<TG>::get(kr + e) + gk[t][e]);
+          GradIO<TG>::put(vr + e, GradIO<TG>::get(vr + e) + gv[t][e]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();

@@ -206,6 +206,8 @@ UNF = [
     (dict(n_sink=4, chunk_len=4, gists=1, window=16, top_k=3), 4 + 200 * 5 + 3, 2, 6, 2, 128, 0),
     (dict(n_sink=16, chunk_len=8, gists=1, window=40, top_k=16), 16 + 120 * 9 + 5, 1, 4, 2, 128, 0),
     (dict(n_sink=2, chunk_len=3, gists=2, window=7, top_k=8), 2 + 150 * 5 + 1, 1, 8, 2, 64, 101),
+    (dict(n_sink=8, chunk_len=16, gists=1, window=24, top_k=4), 8 + 40 * 17 + 9, 1, 4, 1, 64, 0),
+    (dict(n_sink=3, chunk_len=2, gists=1, window=12, top_k=6), 3 + 300 * 3 + 2, 1, 3, 1, 128, 0),
 ]
 
 
