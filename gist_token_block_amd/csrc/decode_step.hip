@@ -18,13 +18,16 @@
 //     gists), the sinks and the window; one MFMA product per 16 rows gives the
 //     logits of all query heads, which feed both the attention partial and,
 //     summed over the heads, the candidates' scores.  Each workgroup keeps the
-//     best k of its candidates.  The last workgroup of a (batch, KV head) to
-//     finish merges those lists into the top-level selection; with two levels
-//     it then streams the kept groups' level-1 gists (scoring and attending
-//     them) and picks the chunks.
-//   phase B (k_step_b, many workgroups per (batch, KV head)): stream the raw
-//     rows of the unfolded chunks; the last workgroup merges the partials of
-//     both phases with log-sum-exp weights and writes the output.
+//     best k of its candidates.  With two levels the last workgroup of a
+//     (batch, KV head) to finish merges those lists into the group selection,
+//     streams the kept groups' level-1 gists (scoring and attending them) and
+//     picks the chunks.
+//   phase B (k_step_b, many workgroups per (batch, KV head)): with one level,
+//     every workgroup merges phase A's lists into the selection itself (one
+//     load of a few lists, where it would otherwise read the selection), so
+//     phase A ends without a completion count; then stream the raw rows of
+//     the unfolded chunks; the last workgroup merges the partials of both
+//     phases with log-sum-exp weights and writes the output.
 // Rows inside the window are attended only by the window segment, so every
 // row is counted once; top-level gists inside the window are still scored.
 #include <limits.h>
@@ -156,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void k_step_a(StepArgs a) {
     }
   }
 
-  // the last split of this (batch, KV head) makes the selection
+  // one level: phase B merges the lists.  Two levels: the last split of this
+  // (batch, KV head) makes the group selection and runs the level-1 stage.
+  if (!two) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -200,15 +205,6 @@ __global__ __launch_bounds__(kThreads) void k_step_a(StepArgs a) {
     nkept = lds_i[0];
   }
   float* extra = gpart + (size_t)a.nsa * G * (D + kPartExtra);
-  if (!two) {
-    if (tid == 0) __hip_atomic_store(&a.counters[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // no level-1 stage: an empty partial in the extra slot
-    for (int x = tid; x < G * (D + kPartExtra); x += kThreads) {
-      const int dd = x % (D + kPartExtra);
-      st_dev(&extra[x], dd == D ? kNegBig : 0.f);
-    }
-    return;
-  }
 
   // two levels: the level-1 gists of the kept groups, scored and (before the
   // window) attended; candidates are every chunk of a kept group (complete,
@@ -267,7 +263,9 @@ __global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
   __shared__ int rowpos[2][kRows], rowflag[3][kRows];
   __shared__ float wstat[192];
   __shared__ int seg_start[65], seg_base[64];
+  __shared__ int chosen[64];
   __shared__ int nseg, am_last;
+  const bool two = l.G2 > 0;
 
   // q first: its loads are in flight while the selection is read
   bf16x8 qreg[C::KS];
@@ -276,9 +274,35 @@ __global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
   // laid out by an exclusive scan over the selection (lanes of wave 0)
   if (wave == 0) {
     const int nch = count_below(l, K_GIST, i) / l.g;   // complete chunks
+    int m = -1;
+    if (!two) {
+      // one level: merge phase A's best-first lists, then the chosen chunks
+      // ascending (split 0 also writes them out)
+      float rs = -__builtin_inff();
+      int ri = INT_MAX;
+      const float* gls = a.list_s + gidx * a.nsa * 64;
+      const int* gli = a.list_i + gidx * a.nsa * 64;
+      for (int sp = 0; sp < a.nsa; ++sp) {
+        const float xs = gls[sp * 64 + lane];
+        const int xi = gli[sp * 64 + lane];
+        if (sp == 0) {
+          rs = xs;
+          ri = xi;
+        } else {
+          wave_merge(rs, ri, xs, xi);
+        }
+      }
+      place_ascending(lane < l.k ? ri : INT_MAX, l.k, chosen, nullptr);
+      __builtin_amdgcn_wave_barrier();
+      if (lane < l.k) {
+        m = chosen[lane];
+        if (split == 0) a.sel[gidx * l.k + lane] = m;
+      }
+    } else if (lane < l.k) {
+      m = a.sel[gidx * l.k + lane];
+    }
     int len = 0, st = 0;
     if (lane < l.k) {
-      const int m = a.sel[gidx * l.k + lane];
       if (m >= 0 && m < nch) {
         st = pos_of(l, K_RAW, m * l.c);
         len = iclamp(lo - st, 0, l.c);
@@ -336,7 +360,9 @@ __global__ __launch_bounds__(kThreads) void k_step_b(StepArgs a) {
   __syncthreads();
   if (!am_last) return;
   // merge every slot (phase A splits, the level-1 slot, phase B splits)
-  merge_partials<D, TO>(gpart, a.nslot, G, reinterpret_cast<TO*>(a.o), a.osb, a.osh, a.lse, a.Hq, b, h);
+  // (one level has no level-1 partial: its slot, a.nsa, is skipped)
+  merge_partials<D, TO>(gpart, a.nslot, G, reinterpret_cast<TO*>(a.o), a.osb, a.osh, a.lse, a.Hq, b, h,
+                        two ? -1 : a.nsa);
   if (tid == 0) __hip_atomic_store(&cnt[gidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -261,11 +261,12 @@ __device__ void rank_candidates(int ncand, ScoreFn score, IdFn id, float* lds_s,
 }
 
 // Merges the nslot partials of one (batch, KV head) at gpart ([nslot][G][D +
-// kPartExtra], device-scope loads) with log-sum-exp weights and writes the
-// output rows of the group's G query heads (and their log-sum-exp).
+// kPartExtra], device-scope loads; slot `skip`, if in range, is not one) with
+// log-sum-exp weights and writes the output rows of the group's G query heads
+// (and their log-sum-exp).
 template <int D, typename TO>
 __device__ void merge_partials(const float* __restrict__ gpart, int nslot, int G, TO* __restrict__ o, int64_t osb,
-                               int64_t osh, float* __restrict__ lse, int Hq, int b, int h) {
+                               int64_t osh, float* __restrict__ lse, int Hq, int b, int h, int skip = -1) {
   const int tid = threadIdx.x;
   constexpr int PS = D + kPartExtra;
   for (int x = tid; x < G * D; x += kThreads) {
@@ -284,14 +285,14 @@ __device__ void merge_partials(const float* __restrict__ gpart, int nslot, int G
       float mb = Mr;
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if (sp0 + j < nslot) mb = fmaxf(mb, pm[j]);
+        if (sp0 + j < nslot && sp0 + j != skip) mb = fmaxf(mb, pm[j]);
       const float al = __builtin_amdgcn_exp2f(Mr - mb);
       Lr *= al;
       LEr *= al;
       Or *= al;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (sp0 + j < nslot) {
+        if (sp0 + j < nslot && sp0 + j != skip) {
           const float wgt = __builtin_amdgcn_exp2f(pm[j] - mb);
           Lr = fmaf(pl[j], wgt, Lr);
           LEr = fmaf(pe[j], wgt, LEr);
