@@ -205,15 +205,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
       // load is a wave-uniform base (row block it) plus a 32-bit lane offset.
       const int p0 = sm.base + u0 * sm.stride1;
       const unsigned kstep = (unsigned)(sm.stride1 * kst) * 2u, vstep = (unsigned)(sm.stride1 * vst) * 2u;
+      // one 64-bit base per tile; the row block and the lane are a 32-bit offset
+      const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)p0 * kst);
+      const char* vbase = reinterpret_cast<const char*>(vb + (int64_t)p0 * vst);
 #pragma unroll
       for (int it = 0; it < C::NIW; ++it) {
         const int wi = wv * C::NIW + it;
-        const char* kbase = reinterpret_cast<const char*>(kb + (int64_t)p0 * kst) +
-                            (size_t)wi * C::RPI * kstep;
-        const char* vbase = reinterpret_cast<const char*>(vb + (int64_t)p0 * vst) +
-                            (size_t)wi * C::RPI * vstep;
-        const unsigned klane = (unsigned)srow * kstep + 2u * (unsigned)koff[it];
-        const unsigned vlane = (unsigned)srow * vstep + 2u * (unsigned)voff[it];
+        const unsigned rows = (unsigned)(wi * C::RPI);
+        const unsigned klane = (rows + (unsigned)srow) * kstep + 2u * (unsigned)koff[it];
+        const unsigned vlane = (rows + (unsigned)srow) * vstep + 2u * (unsigned)voff[it];
         __builtin_amdgcn_global_load_lds((glb_void_ptr)(kbase + klane), (lds_void_ptr)(Kd + wi * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((glb_void_ptr)(vbase + vlane), (lds_void_ptr)(Vd + wi * 512), 16, 0, 0);
       }
