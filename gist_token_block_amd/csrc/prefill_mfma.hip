@@ -273,11 +273,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     // idx - 1, whose buffers the next fetch overwrites.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (idx + 1 < cnt) {
-      fetch(kt_next, Kn, Vn, nslot, nkind, nu0, nwidth);
-      ncode = codes[kt_next];
-      if (idx + 2 < cnt) kt_next = list[idx + 2];
-    }
 
     // ---- S^T = K Q^T: keys 0..31 into s0 first, then keys 32..63 into s1, so
     // the softmax of the first half can start while the second half's MFMAs run.
@@ -303,6 +298,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill_mfma(
     for (int ks = 0; ks < C::KS; ++ks) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // each first-half MFMA, then
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // a second-half read (it may reuse the MFMA's operand registers)
+    }
+    // The next tile's copies go out behind this tile's QK products: the
+    // scalar tile lookup and the address arithmetic fill the gaps of the
+    // dependent MFMA chain instead of following every wave's barrier.
+    if (idx + 1 < cnt) {
+      fetch(kt_next, Kn, Vn, nslot, nkind, nu0, nwidth);
+      ncode = codes[kt_next];
+      if (idx + 2 < cnt) kt_next = list[idx + 2];
     }
 
     // ---- mask (PARTIAL or short tiles only); lane holds keys 8(j/4)+4h2+j%4 (+32)
