@@ -110,7 +110,6 @@ extern "C" gsa_status gsa_build_block_mask(const int8_t* flags, int32_t B, int32
                                            int32_t w, int32_t seq_len, int32_t q_begin, int32_t q_len,
                                            int32_t block_m, int32_t block_n, int8_t* table, int32_t* tile_cnt,
                                            int32_t* tile_list, void* stream) {
-  if (!flags || !table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "NULL pointer argument");
   if (B < 1 || block < 1 || block_m < 1 || block_n < 1 || w < 0)
     return fail(GSA_EINVAL, "B=%d block=%d block_m=%d block_n=%d w=%d", B, block, block_m, block_n, w);
   if (seq_len < 1 || n_blocks != (seq_len + block - 1) / block)
@@ -120,7 +119,8 @@ extern "C" gsa_status gsa_build_block_mask(const int8_t* flags, int32_t B, int32
   if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
     return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
   if (q_begin % block_m) return fail(GSA_EUNSUPPORTED, "q_begin %d is not a multiple of block_m %d", q_begin, block_m);
-  if (q_len == 0) return GSA_OK;
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
+  if (!flags || !table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "NULL pointer argument");
   const int nqt = (q_len + block_m - 1) / block_m;
   const int nkt = (seq_len + block_n - 1) / block_n;
   hipLaunchKernelGGL(k_block_mask_table, dim3(nqt, B), dim3(64), 0, (hipStream_t)stream, flags, n_blocks, block, w,

@@ -182,6 +182,7 @@ extern "C" gsa_status gsa_build_layout(const gsa_layout* layout, int32_t seq_len
   if (block_m < 1 || block_m > 4096) return fail(GSA_EINVAL, "block_m %d outside [1, 4096]", block_m);
   if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
     return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
   if (n_tables < 1) return fail(GSA_EINVAL, "n_tables %d < 1", n_tables);
   const bool fixed = l.k == 0 && l.G2 == 0;
   if (fixed && (sel || sel_groups)) return fail(GSA_EINVAL, "sel given for the fixed layout");
@@ -190,7 +191,6 @@ extern "C" gsa_status gsa_build_layout(const gsa_layout* layout, int32_t seq_len
   if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
   if (l.k > 64 || l.k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
   if (!table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "output pointer is NULL");
-  if (q_len == 0) return GSA_OK;
   const int nqt = (q_len + block_m - 1) / block_m;
   const size_t shm = (size_t)block_m * (sizeof(int) * 6 + sizeof(int) * (l.k + l.k2));
   if (shm > 64 * 1024) return fail(GSA_EUNSUPPORTED, "block_m %d too large for the selection sizes", block_m);

@@ -470,6 +470,9 @@ gsa_status prefill_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, 
   Lay l;
   gsa_status st = make_lay(layout, seq_len, block_n, &l);
   if (st != GSA_OK) return st;
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
   if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
   if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
   if ((st = check_tensor("v", v, d)) != GSA_OK) return st;
@@ -490,7 +493,6 @@ gsa_status prefill_common(const gsa_layout* layout, gsa_tensor q, gsa_tensor k, 
   if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
   if (l.k > 64 || l.k2 > 64) return fail(GSA_EUNSUPPORTED, "top_k and l2_top_k are limited to 64");
   if (!table || !tile_cnt || !tile_list) return fail(GSA_EINVAL, "table pointers are NULL");
-  if (q_len == 0) return GSA_OK;
   const int nqt = (q_len + block_m - 1) / block_m;
   hipStream_t s = (hipStream_t)stream;
   const bool mfma = q.dtype == GSA_BF16 && (d == 64 || d == 128);
@@ -582,6 +584,9 @@ extern "C" gsa_status gsa_attn_prefill_unfolded(const gsa_layout* layout, gsa_te
   fixed_layout.top_k = 0;
   Lay lf;
   if ((st = make_lay(&fixed_layout, seq_len, block_n, &lf)) != GSA_OK) return st;
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
   if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
   if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
   if ((st = check_tensor("v", v, d)) != GSA_OK) return st;
@@ -602,7 +607,6 @@ extern "C" gsa_status gsa_attn_prefill_unfolded(const gsa_layout* layout, gsa_te
   const size_t need = gsa_prefill_unfolded_workspace_bytes(B, Hq, d, q_len);
   if (!ws || ws_bytes < need) return fail(GSA_EINVAL, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GSA_EINVAL, "workspace must be 256-byte aligned");
-  if (q_len == 0) return GSA_OK;
   hipStream_t s = (hipStream_t)stream;
   float* part = (float*)ws;
   if ((st = launch_unfold(l, d, q, k, v, B, Hq, Hkv, q_begin, q_len, sel, scale, part, s)) != GSA_OK) return st;

@@ -258,6 +258,9 @@ extern "C" gsa_status gsa_score_select(const gsa_layout* layout, gsa_tensor q, g
   Lay l;
   gsa_status st = make_lay(layout, seq_len, 64, &l);
   if (st != GSA_OK) return st;
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
   if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
   if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
   if (q.dtype != k.dtype) return fail(GSA_EINVAL, "q and k dtypes differ");
@@ -271,7 +274,6 @@ extern "C" gsa_status gsa_score_select(const gsa_layout* layout, gsa_tensor q, g
   if (!sel) return fail(GSA_EINVAL, "sel is NULL");
   if (l.G2 > 0 && !sel_groups) return fail(GSA_EINVAL, "sel_groups is NULL with two levels");
   if (l.G2 == 0 && sel_groups) return fail(GSA_EINVAL, "sel_groups given for a single level");
-  if (q_len == 0) return GSA_OK;
   const int ncols = gsa_score_columns(layout, seq_len);
   hipStream_t s = (hipStream_t)stream;
   if (q.dtype == GSA_F32) {

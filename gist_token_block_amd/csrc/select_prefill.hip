@@ -283,6 +283,9 @@ extern "C" gsa_status gsa_select_prefill(const gsa_layout* layout, gsa_tensor q,
   if (l.G2 != 0) return fail(GSA_EUNSUPPORTED, "gsa_select_prefill takes one level (gsa_score_select does two)");
   if (l.g != 1) return fail(GSA_EUNSUPPORTED, "gsa_select_prefill takes one gist per chunk (gsa_score_select any)");
   if (l.k < 1 || l.k > 32) return fail(GSA_EUNSUPPORTED, "top_k %d outside [1, 32]", l.k);
+  if (q_begin < 0 || q_len < 0 || q_begin + q_len > seq_len)
+    return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
+  if (q_len == 0) return GSA_OK;   // empty query range: no pointer is read
   if ((st = check_tensor("q", q, d)) != GSA_OK) return st;
   if ((st = check_tensor("k", k, d)) != GSA_OK) return st;
   if (q.dtype != GSA_BF16 || k.dtype != GSA_BF16) return fail(GSA_EUNSUPPORTED, "gsa_select_prefill takes bf16");
@@ -292,7 +295,6 @@ extern "C" gsa_status gsa_select_prefill(const gsa_layout* layout, gsa_tensor q,
     return fail(GSA_EINVAL, "query rows [%d, %d) outside [0, %d)", q_begin, q_begin + q_len, seq_len);
   if (!sel) return fail(GSA_EINVAL, "sel is NULL");
   if (!(scale > 0.f)) return fail(GSA_EINVAL, "scale must be > 0");
-  if (q_len == 0) return GSA_OK;
   const int nqt = (q_len + kBM - 1) / kBM;
   const long long total = (long long)B * Hkv * nqt;
   if (total > 0x7fffffff) return fail(GSA_EUNSUPPORTED, "grid too large");

@@ -33,6 +33,10 @@
  *     next synchronisation.
  *   - Every argument is checked before anything is enqueued: GSA_EINVAL means
  *     nothing was launched; gsa_last_error() gives the reason (thread-local).
+ *   - An empty query range (q_len = 0) in the table, selection and prefill
+ *     entry points returns GSA_OK once the layout and the range are valid,
+ *     without reading any other argument (zero-size tensors may have NULL
+ *     pointers).  The backward entry points require q_len >= 1.
  *   - Integer index outputs are int32, ascending, padded with -1.
  *   - Tensors are described by gsa_tensor: element strides for batch, token
  *     position and head; the head dimension d is contiguous.  Pointers must be

@@ -153,3 +153,31 @@ def test_block_mask_arguments_rejected_before_launch(lib):
     t16 = gsa.Tensor(16, gsa.GSA_BF16, 0, 0, 0, 0)
     assert lib.gsa_attn_prefill_blockmask(t16, t16, t16, t16, None, 1, 1, 1, 64, 512, 0, 512, p, p, p, 64, 64,
                                           0.1, None) == gsa.GSA_EINVAL
+
+
+def test_empty_query_range_is_a_no_op(lib):
+    """q_len = 0: GSA_OK once the layout and the range are valid, with NULL
+    tensors and outputs (nothing is launched, so this runs without a GPU);
+    an invalid layout or range is still rejected."""
+    L = gsa.make_layout
+    sel_lay = L(dict(n_sink=4, chunk_len=4, window=8, top_k=2))
+    fixed = L(dict(n_sink=4, chunk_len=4, window=8))
+    null = gsa.Tensor(None, gsa.GSA_BF16, 0, 0, 0, 0)
+    assert lib.gsa_build_layout(ctypes.byref(sel_lay), 50, 10, 0, 128, 64, None, None, 1, None, None, None,
+                                None) == gsa.GSA_OK
+    assert lib.gsa_score_select(ctypes.byref(sel_lay), null, null, 1, 2, 1, 128, 50, 10, 0, 0.1, None, None,
+                                None, None) == gsa.GSA_OK
+    assert lib.gsa_select_prefill(ctypes.byref(sel_lay), null, null, 1, 2, 1, 128, 50, 0, 0, 0.1, None,
+                                  None) == gsa.GSA_OK
+    assert lib.gsa_attn_prefill(ctypes.byref(fixed), null, null, null, null, None, 1, 2, 1, 128, 50, 50, 0,
+                                None, None, None, None, None, 128, 64, 0.1, None) == gsa.GSA_OK
+    assert lib.gsa_attn_prefill_unfolded(ctypes.byref(sel_lay), null, null, null, null, None, 1, 2, 1, 128, 50,
+                                         0, 0, None, None, None, None, 128, 64, 0.1, None, 0, None) == gsa.GSA_OK
+    assert lib.gsa_build_block_mask(None, 1, 1, 128, 2, 100, 0, 0, 128, 64, None, None, None,
+                                    None) == gsa.GSA_OK
+    # the range and the layout are still checked
+    assert lib.gsa_attn_prefill(ctypes.byref(fixed), null, null, null, null, None, 1, 2, 1, 128, 50, 51, 0,
+                                None, None, None, None, None, 128, 64, 0.1, None) == gsa.GSA_EINVAL
+    bad = L(dict(n_sink=0, chunk_len=0))
+    assert lib.gsa_build_layout(ctypes.byref(bad), 50, 0, 0, 128, 64, None, None, 1, None, None, None,
+                                None) == gsa.GSA_EINVAL
