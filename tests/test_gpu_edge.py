@@ -1,8 +1,9 @@
-"""GPU parity on degenerate inputs: a sequence shorter than the sinks, no
-complete chunk, a window of 0 (the query sees only itself beyond sinks and
-gists), a single position, fewer candidate chunks than top_k, no sinks, and
-an empty query range; decode of a one-position cache and of a cache still
-inside the sinks.  Every row is checked against the fp64 oracle."""
+"""GPU parity on degenerate and extreme inputs: a sequence shorter than the
+sinks, no complete chunk, a window of 0 (the query sees only itself beyond
+sinks and gists), a single position, fewer candidate chunks than top_k, no
+sinks, the largest top_k (64, and 32 groups kept at level 2), and an empty
+query range; decode of a one-position cache and of a cache still inside the
+sinks.  Every row is checked against the fp64 oracle."""
 import math
 
 import numpy as np
@@ -27,6 +28,10 @@ EDGE_PREFILL = [
     (dict(n_sink=64, chunk_len=4, gists=1, window=16, top_k=0), 40, 1, 2, 1, 64, "f32"),
     (dict(n_sink=3, chunk_len=4, gists=1, window=0, top_k=2, l2_chunks=2, l2_gists=1, l2_top_k=1),
      3 + 4 * 11 + 5, 1, 2, 1, 128, "bf16"),
+    # the largest selections the library takes: top_k 64; two levels with 32 groups kept
+    (dict(n_sink=4, chunk_len=4, gists=1, window=8, top_k=64), 4 + 200 * 5 + 3, 1, 4, 2, 128, "bf16"),
+    (dict(n_sink=2, chunk_len=2, gists=1, window=4, top_k=64, l2_chunks=4, l2_gists=1, l2_top_k=32),
+     2 + 80 * 13 + 5, 1, 2, 1, 128, "bf16"),
 ]
 
 
