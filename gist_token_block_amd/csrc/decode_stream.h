@@ -222,10 +222,13 @@ __device__ void store_partial(const f32x4* oacc, float m_run, float l_run, float
 }
 
 // Best-first top list of candidates [0, ncand) scored by score(e) with ids
-// id(e), merged across the 4 waves; wave 0's lanes hold the result (rs, ri).
+// id(e), merged across the waves that hold candidates; wave 0's lanes hold
+// the result (rs, ri).  With at most 64 candidates wave 0 holds them all and
+// nothing is merged (no barrier either).
 template <typename ScoreFn, typename IdFn>
 __device__ void rank_candidates(int ncand, ScoreFn score, IdFn id, float* lds_s, int* lds_i, float& rs, int& ri) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int na = imin(4, (ncand + 63) / 64);   // waves holding candidates
   rs = -__builtin_inff();
   ri = INT_MAX;
   bool empty = true;
@@ -246,12 +249,13 @@ __device__ void rank_candidates(int ncand, ScoreFn score, IdFn id, float* lds_s,
       wave_merge(rs, ri, s, d);
     }
   }
+  if (na <= 1) return;
   __syncthreads();
   lds_s[wave * 64 + lane] = rs;
   lds_i[wave * 64 + lane] = ri;
   __syncthreads();
-  for (int st = 1; st < 4; st <<= 1) {
-    if ((wave & (2 * st - 1)) == 0 && wave + st < 4) {
+  for (int st = 1; st < na; st <<= 1) {
+    if ((wave & (2 * st - 1)) == 0 && wave + st < na) {
       wave_merge(rs, ri, lds_s[(wave + st) * 64 + lane], lds_i[(wave + st) * 64 + lane]);
       lds_s[wave * 64 + lane] = rs;
       lds_i[wave * 64 + lane] = ri;
