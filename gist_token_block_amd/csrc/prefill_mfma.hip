@@ -81,12 +81,12 @@ template <> struct OutStore<unsigned short> {
 // INIT: each row starts from a softmax partial over keys outside the table
 // (init [B, q_len, Hq, D + 3]: unnormalised O, max in log2 units, sums) --
 // the raw tokens its chosen chunks unfold -- instead of from zero.
-// Waves per SIMD: 2 at d = 128 (256 VGPRs); 3 at d = 64, where the tile's
-// products are half as long against the same softmax work and the third wave
-// fits in 168 VGPRs and the LDS of three workgroups (gzip block-mask workload
-// 0.748 -> 0.647 ms).
+// Waves per SIMD: 2 at d = 128 (256 VGPRs).  At d = 64 a tile's products are
+// half as long against the same softmax work, and more waves hide more of it:
+// 4 (128 VGPRs, the LDS of four workgroups; gzip block-mask workload 0.748 ->
+// 0.626 ms), or 3 (168 VGPRs) with the LSE, whose extra sum spills at 128.
 template <int D, typename TO, bool LSE, bool INIT>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void k_prefill_mfma(
+__global__ __launch_bounds__(kThreads, D == 64 ? (LSE ? 3 : 4) : 2) void k_prefill_mfma(
     Lay l, const unsigned short* __restrict__ q, int64_t qsb, int64_t qst, int64_t qsh,
     const unsigned short* __restrict__ k, int64_t ksb, int64_t kst, int64_t ksh,
     const unsigned short* __restrict__ v, int64_t vsb, int64_t vst, int64_t vsh, TO* __restrict__ o,
